@@ -1,0 +1,218 @@
+"""Benchmark of the whole sparse self-attention step on one MI355X.
+
+One step = QK-RMSNorm + 3D-RoPE, reorder of Q', K' and V, block selection,
+block-sparse attention and the inverse reorder of O, on synthetic inputs
+already resident in HBM.  Default workload: Wan2.1-14B-like 720p latent
+grid 21×45×80 = 75,600 tokens, 40 heads, d 128, 128-token blocks,
+sparsity 0.75, same-frame key blocks always kept.
+
+Prints one JSON line.  ``value`` is the executed attention work of a step
+(4·block²·d flops per kept block pair) divided by the whole step's time;
+the attention kernel alone is reported in ``roofline`` against the bf16
+dense MFMA peak, timed with HIP events on the stream it runs on.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+step and scales it to the same unit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "executed attn TFLOP/s (% bf16 MFMA peak) + ms/layer at 75.6k tokens, sp=0.75"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan720p_sp75")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-qblocks", type=int, default=256,
+                    help="query blocks of one head the oracle's attention runs on")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the path shards by head with no exchange, "
+              "and multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_qk_amd as S
+    from block_sparse_attention_qk_amd import inputs as I
+
+    wl = I.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    q, k, v = (I.full_tensor(wl, t) for t in (I.TENSOR_Q, I.TENSOR_K, I.TENSOR_V))
+    wq, wk = I.norm_weights(wl)
+    print(f"inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    dwq, dwk = torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda()
+    plan = S.sva_plan_create_ex(S.desc_for(wl))
+    info = plan.info
+    buf = S.Buffers(plan)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        # ev: 8 events bracketing the stages of this step
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
+        S.sva_qk_norm_rope(plan, dq, dk, dwq, dwk, buf.qn, buf.kn)
+        rec(1)
+        S.sva_reorder(plan, buf.qn, buf.q_r, S.SVA_FORWARD)
+        S.sva_reorder(plan, buf.kn, buf.k_r, S.SVA_FORWARD)
+        rec(2)
+        S.sva_reorder(plan, dv, buf.v_t, S.SVA_FORWARD_VT)
+        rec(3)
+        if not info.dense:
+            S.sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col)
+        rec(4)
+        S.sva_attention(plan, buf.q_r, buf.k_r, buf.v_t, buf.col, buf.o_r)
+        rec(5)
+        S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
+        rec(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, per-stage HIP events on the stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    names = ["prologue", "reorder_qk", "reorder_v", "select", "attention", "reorder_o"]
+    stage = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
+             for i, n in enumerate(names)}
+
+    b, d, H, B = wl.block, wl.d, wl.H, wl.B
+    nnz = int(info.nnz)
+    attn_flop = 4.0 * b * b * d * nnz
+    attn_ms = stage["attention"]
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    value = attn_flop / (ms_step * 1e-3) / 1e12
+    N, Np, nB = int(info.N), int(info.Np), int(info.nB)
+    pro_bytes = 4.0 * B * N * H * d * 2
+    sel_bytes = 2.0 * B * H * Np * d * 2 + 2.0 * B * H * nB * d * 8 + 4.0 * nnz
+    stage_gbs = {
+        "prologue": pro_bytes / (stage["prologue"] * 1e-3) / 1e9,
+        "reorder_qk": 2 * (B * H * (N + Np) * d * 2) / (stage["reorder_qk"] * 1e-3) / 1e9,
+        "reorder_v": (B * H * (N + Np) * d * 2) / (stage["reorder_v"] * 1e-3) / 1e9,
+        "reorder_o": (B * H * (N + Np) * d * 2) / (stage["reorder_o"] * 1e-3) / 1e9,
+    }
+    if not info.dense:
+        stage_gbs["select"] = sel_bytes / (stage["select"] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "B": B, "H": H, "d": d,
+            "grid": f"{wl.T}x{wl.Hh}x{wl.W}", "tokens": N, "n_extra": wl.n_extra,
+            "block": b, "sparsity": wl.sparsity, "keep_same_frame": bool(wl.flags & I.KEEP_SAME_FRAME),
+            "dense": bool(info.dense), "kept_block_pairs": nnz,
+            "executed_attn_tflop": round(attn_flop / 1e12, 3),
+        },
+        "roofline": {
+            "kernel": "attn_kernel<128,128>" if (d == 128 and b == 128) else f"attn_kernel<{d},{b}>",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "stages_ms": {n: round(t, 4) for n, t in stage.items()},
+        "stages_hbm_gbs": {n: round(t, 1) for n, t in stage_gbs.items()},
+        "attn_ms": round(attn_ms, 4),
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, wq, wk, info, args.cpu_qblocks, ms_step)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, q, k, v, wq, wk, info, nq, gpu_ms):
+    """Time the CPU oracle on a bounded sample: head 0's whole prologue,
+    reorder and selection, plus attention for `nq` query blocks of it;
+    extrapolate to the full step (× heads, × query blocks) and express the
+    result in the same unit as ``value``."""
+    import numpy as np
+    import oracle.sva_oracle as O
+
+    g = O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
+                   sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+    cores = len(os.sched_getaffinity(0))
+    nq = min(nq, g.nB)
+    qblocks = np.linspace(0, g.nB - 1, nq).astype(int).tolist()
+    t0 = time.perf_counter()
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    t1 = time.perf_counter()
+    qh = O.bf16_bits_to_f64(q[0, :, 0])
+    kh = O.bf16_bits_to_f64(k[0, :, 0])
+    vh = O.bf16_bits_to_f64(v[0, :, 0])
+    r = O.run_head(qh, kh, vh, wq[0], wk[0], g, qblocks=[], perm=perm, meta=meta)
+    t2 = time.perf_counter()
+    O.block_attention(r["qr"], r["kr"], r["vr"], r["kept"], g, meta, qblocks=qblocks)
+    t3 = time.perf_counter()
+    per_head = (t2 - t1) + (t3 - t2) * g.nB / nq
+    layer_s = (t1 - t0) + per_head * wl.H * wl.B
+    attn_flop = 4.0 * g.block ** 2 * g.d * int(info.nnz)
+    return {
+        "value": round(attn_flop / layer_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"head 0 of {wl.H}: prologue, reorder, pooling and selection over all "
+                   f"{g.nB} query blocks, attention over {nq} of them; measured "
+                   f"{t3 - t0:.1f}s, extrapolated to {layer_s:.1f}s per step "
+                   f"(GPU {gpu_ms:.2f} ms)"),
+        "measured_s": round(t3 - t0, 2),
+        "extrapolated_step_s": round(layer_s, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

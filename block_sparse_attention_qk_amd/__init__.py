@@ -1,0 +1,343 @@
+"""Block-sparse video self-attention on MI355X: thin Python binding.
+
+The functions here carry the same names as the C ABI in ``include/sva.h``
+and only marshal arguments: torch tensors are checked (dtype, device,
+shape, contiguity, alignment) and passed as raw device pointers together
+with the current HIP stream.  Every step runs in the HIP kernels of
+``libsva.so``; there is no fallback path.  The library is loaded on first
+use and a missing or unloadable library raises ``RuntimeError``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsva.so")
+
+SVA_OK = 0
+SVA_ERR_INVALID_ARG = -1
+SVA_ERR_UNSUPPORTED = -2
+SVA_ERR_WORKSPACE = -3
+SVA_ERR_HIP = -4
+
+SVA_DENSE = 1
+SVA_KEEP_SAME_FRAME = 2
+
+SVA_FORWARD = 0
+SVA_INVERSE = 1
+SVA_FORWARD_VT = 2
+
+EXPORTED = (
+    "sva_plan_desc_init", "sva_plan_query", "sva_plan_host_tables",
+    "sva_plan_create", "sva_plan_create_ex", "sva_plan_get_info", "sva_destroy",
+    "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
+    "sva_status_string", "sva_last_error",
+)
+
+
+class sva_plan_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int),
+        ("T", ctypes.c_int), ("Hh", ctypes.c_int), ("W", ctypes.c_int),
+        ("d", ctypes.c_int), ("block", ctypes.c_int),
+        ("sparsity", ctypes.c_double), ("flags", ctypes.c_uint),
+        ("tile_t", ctypes.c_int), ("tile_h", ctypes.c_int), ("tile_w", ctypes.c_int),
+        ("n_extra", ctypes.c_int),
+        ("rope_theta", ctypes.c_double),
+        ("rope_split", ctypes.c_int * 3),
+        ("eps", ctypes.c_double),
+    ]
+
+
+class sva_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("n_video", ctypes.c_int64), ("N", ctypes.c_int64),
+        ("n_video_pad", ctypes.c_int64), ("Np", ctypes.c_int64),
+        ("nB", ctypes.c_int32), ("nB_video", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("max_row_len", ctypes.c_int32),
+        ("nnz_per_head", ctypes.c_int64), ("nnz", ctypes.c_int64),
+        ("select_workspace_bytes", ctypes.c_size_t),
+        ("dense", ctypes.c_int32),
+        ("tile", ctypes.c_int32 * 3),
+        ("rope_split", ctypes.c_int32 * 3),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsva.so (once).  Raises RuntimeError when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_attention_qk_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, d, u, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_uint, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.sva_plan_desc_init.argtypes = [P(sva_plan_desc), i, i, i, i, i, i, i, d, u]
+    L.sva_plan_query.argtypes = [P(sva_plan_desc), P(sva_plan_info)]
+    L.sva_plan_host_tables.argtypes = [P(sva_plan_desc), vp, vp, vp]
+    L.sva_plan_create.argtypes = [P(vp), i, i, i, i, i, i, i, d, u]
+    L.sva_plan_create_ex.argtypes = [P(vp), P(sva_plan_desc)]
+    L.sva_plan_get_info.argtypes = [vp, P(sva_plan_info)]
+    L.sva_destroy.argtypes = [vp]
+    L.sva_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sva_reorder.argtypes = [vp, vp, vp, i, vp]
+    L.sva_select_blocks.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    L.sva_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.sva_status_string.argtypes = [i]
+    L.sva_status_string.restype = ctypes.c_char_p
+    L.sva_last_error.argtypes = []
+    L.sva_last_error.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("sva_status_string", "sva_last_error"):
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+class SvaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sva status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != SVA_OK:
+        raise SvaError(status, lib().sva_last_error().decode())
+
+
+# --------------------------------------------------------------------------
+# host-only calls
+# --------------------------------------------------------------------------
+
+def sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, flags=0, tile=(0, 0, 0),
+                       n_extra=0, rope_theta=0.0, rope_split=(0, 0, 0), eps=0.0) -> sva_plan_desc:
+    desc = sva_plan_desc()
+    _check(lib().sva_plan_desc_init(ctypes.byref(desc), B, H, T, Hh, W, d, block,
+                                    float(sparsity), flags))
+    desc.tile_t, desc.tile_h, desc.tile_w = tile
+    desc.n_extra = n_extra
+    desc.rope_theta = rope_theta
+    desc.rope_split[:] = list(rope_split)
+    desc.eps = eps
+    return desc
+
+
+def sva_plan_query(desc: sva_plan_desc) -> sva_plan_info:
+    info = sva_plan_info()
+    _check(lib().sva_plan_query(ctypes.byref(desc), ctypes.byref(info)))
+    return info
+
+
+def sva_plan_host_tables(desc: sva_plan_desc, forced: bool = False):
+    """(perm [N] int32, row_ptr [nB+1] int32, forced [nB, nB] uint8 or None)."""
+    info = sva_plan_query(desc)
+    perm = np.empty(info.N, dtype=np.int32)
+    row_ptr = np.empty(info.nB + 1, dtype=np.int32)
+    f = np.empty((info.nB, info.nB), dtype=np.uint8) if forced else None
+    _check(lib().sva_plan_host_tables(ctypes.byref(desc), perm.ctypes.data,
+                                      row_ptr.ctypes.data,
+                                      f.ctypes.data if f is not None else None))
+    return perm, row_ptr, f
+
+
+def desc_for(wl) -> sva_plan_desc:
+    """Plan description of a workload from ``inputs.WORKLOADS``."""
+    return sva_plan_desc_init(wl.B, wl.H, wl.T, wl.Hh, wl.W, wl.d, wl.block, wl.sparsity,
+                              wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+
+
+# --------------------------------------------------------------------------
+# device calls (torch tensors)
+# --------------------------------------------------------------------------
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _tensor(t, shape, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Plan:
+    """A plan on the current device; wraps the C handle."""
+
+    handle: ctypes.c_void_p
+    desc: sva_plan_desc
+    info: sva_plan_info
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.sva_destroy(h)
+            self.handle = None
+
+    # shapes
+    @property
+    def raster_shape(self):
+        d = self.desc
+        return (d.B, int(self.info.N), d.H, d.d)
+
+    @property
+    def tile_shape(self):
+        d = self.desc
+        return (d.B, d.H, int(self.info.Np), d.d)
+
+    @property
+    def vt_shape(self):
+        d = self.desc
+        return (d.B, d.H, int(self.info.nB), d.d, d.block)
+
+    def host_tables(self, forced=False):
+        return sva_plan_host_tables(self.desc, forced)
+
+
+def sva_plan_create(B, H, T, Hh, W, d, block, sparsity, dense_flag=0) -> Plan:
+    return sva_plan_create_ex(sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, dense_flag))
+
+
+def sva_plan_create_ex(desc: sva_plan_desc) -> Plan:
+    h = ctypes.c_void_p()
+    _check(lib().sva_plan_create_ex(ctypes.byref(h), ctypes.byref(desc)))
+    info = sva_plan_info()
+    _check(lib().sva_plan_get_info(h, ctypes.byref(info)))
+    return Plan(h, desc, info)
+
+
+def sva_plan_get_info(plan: Plan) -> sva_plan_info:
+    info = sva_plan_info()
+    _check(lib().sva_plan_get_info(plan.handle, ctypes.byref(info)))
+    return info
+
+
+def sva_destroy(plan: Plan) -> None:
+    if plan.handle is not None and plan.handle.value:
+        _check(lib().sva_destroy(plan.handle))
+    plan.handle = None
+
+
+def sva_qk_norm_rope(plan: Plan, q, k, wq, wk, q_out, k_out, stream=None) -> None:
+    import torch
+    shp = plan.raster_shape
+    wshape = (plan.desc.H, plan.desc.d)
+    args = [
+        _tensor(q, shp, torch.bfloat16, "q"), _tensor(k, shp, torch.bfloat16, "k"),
+        _tensor(wq, wshape, torch.float32, "wq") if wq is not None else None,
+        _tensor(wk, wshape, torch.float32, "wk") if wk is not None else None,
+        _tensor(q_out, shp, torch.bfloat16, "q_out"), _tensor(k_out, shp, torch.bfloat16, "k_out"),
+    ]
+    _check(lib().sva_qk_norm_rope(plan.handle, *args, _stream(stream)))
+
+
+def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
+    import torch
+    if direction == SVA_FORWARD:
+        si, so = plan.raster_shape, plan.tile_shape
+    elif direction == SVA_INVERSE:
+        si, so = plan.tile_shape, plan.raster_shape
+    elif direction == SVA_FORWARD_VT:
+        si, so = plan.raster_shape, plan.vt_shape
+    else:
+        raise ValueError("unknown direction")
+    _check(lib().sva_reorder(plan.handle, _tensor(inp, si, torch.bfloat16, "in"),
+                             _tensor(out, so, torch.bfloat16, "out"), direction, _stream(stream)))
+
+
+def sva_select_blocks(plan: Plan, q_r, k_r, workspace, col, stream=None) -> None:
+    import torch
+    if plan.info.dense:
+        return
+    ts = plan.tile_shape
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().sva_select_blocks(plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r"),
+                                   _tensor(k_r, ts, torch.bfloat16, "k_r"),
+                                   ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
+                                   _tensor(col, (int(plan.info.nnz),), torch.int32, "col"),
+                                   _stream(stream)))
+
+
+def sva_attention(plan: Plan, q_r, k_r, v_t, col, o_r, stream=None) -> None:
+    import torch
+    ts = plan.tile_shape
+    c = None
+    if col is not None:
+        c = _tensor(col, (int(plan.info.nnz),), torch.int32, "col")
+    elif not plan.info.dense:
+        raise ValueError("col is required for a sparse plan")
+    _check(lib().sva_attention(plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r"),
+                               _tensor(k_r, ts, torch.bfloat16, "k_r"),
+                               _tensor(v_t, plan.vt_shape, torch.bfloat16, "v_t"), c,
+                               _tensor(o_r, ts, torch.bfloat16, "o_r"), _stream(stream)))
+
+
+def sva_status_string(status: int) -> str:
+    return lib().sva_status_string(status).decode()
+
+
+def sva_last_error() -> str:
+    return lib().sva_last_error().decode()
+
+
+# --------------------------------------------------------------------------
+# convenience: buffers and the whole step
+# --------------------------------------------------------------------------
+
+class Buffers:
+    """Device buffers for one call of the whole step on a plan."""
+
+    def __init__(self, plan: Plan, device="cuda"):
+        import torch
+        bf = torch.bfloat16
+        self.qn = torch.empty(plan.raster_shape, dtype=bf, device=device)
+        self.kn = torch.empty(plan.raster_shape, dtype=bf, device=device)
+        self.q_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
+        self.k_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
+        self.v_t = torch.empty(plan.vt_shape, dtype=bf, device=device)
+        self.o_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
+        self.o = torch.empty(plan.raster_shape, dtype=bf, device=device)
+        nnz = int(plan.info.nnz) if not plan.info.dense else 0
+        self.col = torch.empty(nnz, dtype=torch.int32, device=device) if nnz else None
+        ws = int(plan.info.select_workspace_bytes)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+
+
+def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
+    """The whole step: prologue, reorders, selection, attention, inverse
+    reorder.  Returns the raster output tensor ``buf.o``."""
+    sva_qk_norm_rope(plan, q, k, wq, wk, buf.qn, buf.kn, stream)
+    sva_reorder(plan, buf.qn, buf.q_r, SVA_FORWARD, stream)
+    sva_reorder(plan, buf.kn, buf.k_r, SVA_FORWARD, stream)
+    sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
+    if not plan.info.dense:
+        sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col, stream)
+    sva_attention(plan, buf.q_r, buf.k_r, buf.v_t, buf.col, buf.o_r, stream)
+    sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
+    return buf.o

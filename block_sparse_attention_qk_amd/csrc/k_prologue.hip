@@ -1,0 +1,144 @@
+// Fused QK-RMSNorm + 3D-RoPE.
+//
+// Follows "MiniMax-H3 在 8×H200 上基准测试", section "内核层": the QK RMSNorm
+// and the 3D RoPE run as one kernel, on the exact rounding path that stores
+// the normalised value (bf16) before rotating it.  Per (token, head) row x:
+//   y = bf16(x · rsqrt(mean(x²) + eps) · w[h]),  out = bf16(rotate(y)),
+// rotate turning channel pairs (2i, 2i+1) of the t/h/w sections by
+// coordinate · theta^(-2i/width) (cos/sin from the plan's tables).
+//
+// Streaming kernel, bound by HBM: every row is read once and written once
+// (4 · rows · d · 2 bytes for Q and K).  d/8 lanes own one row, 16 bytes
+// each, so a wave moves 1 KB of contiguous rows per access; the sum of
+// squares is reduced across the row's lanes with xor shuffles.  Each
+// thread handles kRows rows to keep several loads in flight.
+#include "kernels.h"
+
+namespace sva {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 4;   // rows per thread
+
+struct ProArgs {
+    DevPlan p;
+    const uint16_t* in[2];
+    uint16_t* out[2];
+    const float* w[2];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
+    constexpr int LPR = D / 8;                 // lanes per row
+    constexpr int RPB = kThreads / LPR;        // rows per block per step
+    const int tensor = blockIdx.y;
+    const DevPlan& p = a.p;
+    const uint4* in = reinterpret_cast<const uint4*>(a.in[tensor]);
+    uint4* out = reinterpret_cast<uint4*>(a.out[tensor]);
+    const float* __restrict__ w = a.w[tensor];
+    const int sub = threadIdx.x % LPR;
+    const int64_t rows = (int64_t)p.B * p.N * p.H;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
+
+    uint4 x[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t row = row0 + (int64_t)r * RPB;
+        x[r] = row < rows ? in[row * LPR + sub] : make_uint4(0, 0, 0, 0);
+    }
+    const int hw = p.Hh * p.W;
+    const float inv_d = 1.0f / D;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t row = row0 + (int64_t)r * RPB;
+        const uint32_t u[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16lo(u[e]);
+            v[2 * e + 1] = bf16hi(u[e]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+        if (row >= rows) continue;
+        const int h = (int)(row % p.H);
+        const int64_t n = (row / p.H) % p.N;
+        const float rs = rsqrtf(ss * inv_d + p.eps);
+        float wv[8];
+        if (w) {
+            const float4* wp = reinterpret_cast<const float4*>(w + (int64_t)h * D + sub * 8);
+            const float4 w0 = wp[0], w1 = wp[1];
+            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[e] = 1.f;
+        }
+        // norm, then round to bf16 (the stored value the rotation starts from)
+        uint32_t yb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            yb[e] = pack_bf16x2(v[2 * e] * rs * wv[2 * e], v[2 * e + 1] * rs * wv[2 * e + 1]);
+        uint32_t ob[4];
+        int pos3[3] = {0, 0, 0};
+        const bool video = n < p.n_video;
+        if (video) {
+            const int nn = (int)n;
+            pos3[0] = nn / hw;
+            const int rem = nn - pos3[0] * hw;
+            pos3[1] = rem / p.W;
+            pos3[2] = rem - pos3[1] * p.W;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y0 = bf16lo(yb[e]), y1 = bf16hi(yb[e]);
+            int pi = sub * 4 + e;              // pair index within the row
+            float c = 1.f, s = 0.f;
+            if (video) {
+#pragma unroll
+                for (int ax = 0; ax < 3; ++ax) {
+                    const int half = p.rope_half[ax];
+                    if (pi >= 0 && pi < half) {
+                        const float2 cs = p.rope_cs[p.rope_off[ax] + pos3[ax] * half + pi];
+                        c = cs.x;
+                        s = cs.y;
+                    }
+                    pi -= half;
+                }
+            }
+            ob[e] = pack_bf16x2(y0 * c - y1 * s, y0 * s + y1 * c);
+        }
+        out[row * LPR + sub] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
+                           const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
+                           hipStream_t s) {
+    ProArgs a;
+    a.p = p;
+    a.in[0] = q;
+    a.in[1] = k;
+    a.out[0] = qo;
+    a.out[1] = ko;
+    a.w[0] = wq;
+    a.w[1] = wk;
+    const int64_t rows = (int64_t)p.B * p.N * p.H;
+    const int lpr = p.d / 8;
+    const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
+    const int64_t blocks = (rows + per_block - 1) / per_block;
+    dim3 grid((unsigned)blocks, 2);
+    if (p.d == 128)
+        hipLaunchKernelGGL(prologue_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(prologue_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sva

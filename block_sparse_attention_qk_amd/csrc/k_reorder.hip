@@ -1,0 +1,155 @@
+// 3D-tile token reorder.
+//
+// The permutation gathers the raster video tokens tile by tile so each
+// block of the sequence is a compact space-time patch (the "Sol Video
+// Inference Engine" blog, section 4.2.2, cites Sparse VideoGen2's token
+// permutation for GPU layout; the tile order itself is this library's
+// reading).  Three directions:
+//   forward     raster [B,N,H,d] -> tile order [B,H,Np,d], padding zeroed
+//   inverse     tile order -> raster, padding dropped
+//   forward_vt  raster -> V tiles [B,H,nB,d,block]: each block of V stored
+//               transposed, the layout the attention kernel reads V in
+//               (channel-major rows of `block` keys).
+// All three move every byte once and are bound by HBM bandwidth.  Rows are
+// d·2 = 128 or 256 contiguous bytes, so gathers stay at full-line width.
+#include "kernels.h"
+
+namespace sva {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 4;
+
+// Forward: one output row (b, h, p) per d/8 lanes.
+template <int D>
+__global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const uint4* in,
+                                                               uint4* out) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = kThreads / LPR;
+    const int sub = threadIdx.x % LPR;
+    const int64_t rows = (int64_t)p.B * p.H * p.Np;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
+    uint4 v[kRows];
+    int64_t dst[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t row = row0 + (int64_t)r * RPB;
+        dst[r] = row;
+        v[r] = make_uint4(0, 0, 0, 0);
+        if (row < rows) {
+            const int64_t pos = row % p.Np;
+            const int64_t bh = row / p.Np;
+            const int h = (int)(bh % p.H);
+            const int64_t b = bh / p.H;
+            const int n = p.inv[pos];
+            if (n >= 0) v[r] = in[((b * p.N + n) * p.H + h) * LPR + sub];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+        if (dst[r] < rows) out[dst[r] * LPR + sub] = v[r];
+}
+
+// Inverse: one output raster row (b, n, h) per d/8 lanes; writes are
+// contiguous, reads gather whole rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const uint4* in,
+                                                               uint4* out) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = kThreads / LPR;
+    const int sub = threadIdx.x % LPR;
+    const int64_t rows = (int64_t)p.B * p.N * p.H;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
+    uint4 v[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t row = row0 + (int64_t)r * RPB;
+        if (row < rows) {
+            const int h = (int)(row % p.H);
+            const int64_t bn = row / p.H;
+            const int64_t n = bn % p.N;
+            const int64_t b = bn / p.N;
+            const int64_t pos = p.perm[n];
+            v[r] = in[((b * p.H + h) * p.Np + pos) * LPR + sub];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int64_t row = row0 + (int64_t)r * RPB;
+        if (row < rows) out[row * LPR + sub] = v[r];
+    }
+}
+
+// Forward into V tiles.  One workgroup per (b, h, block): thread (kg, dc)
+// loads keys kg*8..kg*8+7 of channel chunk dc (8 rows of 16 bytes), turns
+// the 8×8 bf16 square around in registers and writes channels dc*8..dc*8+7
+// of those 8 keys (8 rows of 16 bytes of the transposed tile).
+template <int D, int BLK>
+__global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan p,
+                                                                       const uint4* in,
+                                                                       uint4* out) {
+    constexpr int DC = D / 8;      // channel chunks per row
+    const int dc = threadIdx.x % DC;
+    const int kg = threadIdx.x / DC;
+    const int kb = blockIdx.x % p.nB;
+    const int64_t bh = blockIdx.x / p.nB;
+    const int h = (int)(bh % p.H);
+    const int64_t b = bh / p.H;
+    uint32_t m[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t pos = (int64_t)kb * BLK + kg * 8 + j;
+        const int n = p.inv[pos];
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n >= 0) v = in[((b * p.N + n) * p.H + h) * DC + dc];
+        m[j][0] = v.x; m[j][1] = v.y; m[j][2] = v.z; m[j][3] = v.w;
+    }
+    uint4* dst = out + ((bh * p.nB + kb) * D + dc * 8) * (BLK / 8) + kg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t o[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = m[2 * w][e / 2], hi = m[2 * w + 1][e / 2];
+            o[w] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                           : ((lo & 0xffffu) | (hi << 16));
+        }
+        dst[e * (BLK / 8)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
+                          hipStream_t s) {
+    const uint4* i4 = reinterpret_cast<const uint4*>(in);
+    uint4* o4 = reinterpret_cast<uint4*>(out);
+    const int lpr = p.d / 8;
+    const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
+    if (direction == 0) {
+        const int64_t rows = (int64_t)p.B * p.H * p.Np;
+        dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+        if (p.d == 128) hipLaunchKernelGGL(reorder_fwd_kernel<128>, grid, dim3(kThreads), 0, s, p, i4, o4);
+        else hipLaunchKernelGGL(reorder_fwd_kernel<64>, grid, dim3(kThreads), 0, s, p, i4, o4);
+    } else if (direction == 1) {
+        const int64_t rows = (int64_t)p.B * p.N * p.H;
+        dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+        if (p.d == 128) hipLaunchKernelGGL(reorder_inv_kernel<128>, grid, dim3(kThreads), 0, s, p, i4, o4);
+        else hipLaunchKernelGGL(reorder_inv_kernel<64>, grid, dim3(kThreads), 0, s, p, i4, o4);
+    } else {
+        dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
+        const int threads = (p.d / 8) * (p.block / 8);
+        if (p.d == 128 && p.block == 128)
+            hipLaunchKernelGGL((reorder_vt_kernel<128, 128>), grid, dim3(threads), 0, s, p, i4, o4);
+        else if (p.d == 128)
+            hipLaunchKernelGGL((reorder_vt_kernel<128, 64>), grid, dim3(threads), 0, s, p, i4, o4);
+        else if (p.block == 128)
+            hipLaunchKernelGGL((reorder_vt_kernel<64, 128>), grid, dim3(threads), 0, s, p, i4, o4);
+        else
+            hipLaunchKernelGGL((reorder_vt_kernel<64, 64>), grid, dim3(threads), 0, s, p, i4, o4);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sva

@@ -1,0 +1,245 @@
+// Block selection: mean pooling, block scores, top-k per query block.
+//
+// Follows "MiniMax-H3 在 8×H200 上基准测试", section "SubBlock 稀疏注意力如何工作":
+// a lightweight pooling step scores every key block for each query block
+// and head, the best-scored key blocks are kept (sparsity = fraction
+// dropped) and their indices go to the block-sparse kernel; rows are ranked
+// independently per query block and head.  The score here is the plain
+// reading of "mean-pooled Q and K": s(qb, kb) = mean(Q' of qb) · mean(K' of kb).
+//
+// Two kernels:
+//  pool   one workgroup per (tensor, b, h, block): float64 sums of the
+//         valid rows, divided by the valid count.  Sums of at most 128 bf16
+//         values are exact in float64 for the data this sees, so the means
+//         do not depend on summation order.  HBM bound (reads Q' and K'
+//         once).  q means are stored [B,H,nB,d], k means transposed
+//         [B,H,d,nB] so the score loop reads them coalesced.
+//  topk   one workgroup per (b, h, R query blocks): float64 scores of the R
+//         rows against every key block into LDS, then one wave per row
+//         finds the r-th largest eligible score by a bitwise search on
+//         order-preserving 64-bit keys (ballot + popcount, no sorting),
+//         takes equal scores lowest index first, and writes the kept
+//         block indices in ascending order with ballot prefix counts.
+#include "kernels.h"
+
+namespace sva {
+
+namespace {
+
+constexpr int kPoolThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const uint4* qr,
+                                                            const uint4* kr, double* qmean,
+                                                            double* kmeanT) {
+    constexpr int LPR = D / 8;
+    constexpr int RG = kPoolThreads / LPR;   // row groups
+    __shared__ double part[RG][D];
+    const int tensor = blockIdx.y;
+    const int kb = blockIdx.x % p.nB;
+    const int64_t bh = blockIdx.x / p.nB;
+    const uint4* src = (tensor == 0 ? qr : kr) + (bh * p.Np + (int64_t)kb * p.block) * LPR;
+    const int dc = threadIdx.x % LPR;
+    const int rg = threadIdx.x / LPR;
+    const int valid = p.blk_valid[kb];
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = rg; r < valid; r += RG) {
+        const uint4 v = src[(int64_t)r * LPR + dc];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)bf16lo(u[e]);
+            acc[2 * e + 1] += (double)bf16hi(u[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][dc * 8 + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        double s = 0.0;
+#pragma unroll 4
+        for (int g = 0; g < RG; ++g) s += part[g][threadIdx.x];
+        const double mean = s / (double)valid;
+        if (tensor == 0)
+            qmean[(bh * p.nB + kb) * D + threadIdx.x] = mean;
+        else
+            kmeanT[(bh * D + threadIdx.x) * p.nB + kb] = mean;
+    }
+}
+
+constexpr int kTopkThreads = 256;
+constexpr int kScoreLds = 65536;   // bytes of LDS for the q means and score rows
+
+__device__ __forceinline__ uint64_t order_key(double s) {
+    // canonical +0, then flip so unsigned order = numeric order
+    const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = __shfl_xor(v, m, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = __shfl_xor(v, m, 64);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+template <int D, int NSLOT>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const double* qmean,
+                                                            const double* kmeanT, int R,
+                                                            int32_t* col) {
+    extern __shared__ double smem[];
+    double* qs = smem;                 // [R][D]
+    double* sc = smem + R * D;         // [R][nB]
+    const int nB = p.nB;
+    const int groups = (nB + R - 1) / R;
+    const int g = blockIdx.x % groups;
+    const int64_t bh = blockIdx.x / groups;
+    const int qb0 = g * R;
+    const int nrows = min(R, nB - qb0);
+
+    for (int i = threadIdx.x; i < nrows * D; i += kTopkThreads)
+        qs[i] = qmean[(bh * nB + qb0) * D + i];
+    __syncthreads();
+
+    // scores: thread per key block, R rows at once (R <= 8)
+    const double* kt = kmeanT + bh * D * (int64_t)nB;
+    for (int kb = threadIdx.x; kb < nB; kb += kTopkThreads) {
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int dd = 0; dd < D; ++dd) {
+            const double kv = kt[(int64_t)dd * nB + kb];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r < nrows) acc[r] = fma(qs[r * D + dd], kv, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r < nrows) sc[r * nB + kb] = acc[r];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+    for (int r = wave; r < nrows; r += kTopkThreads / 64) {
+        const int qb = qb0 + r;
+        const int len = p.row_ptr[qb + 1] - p.row_ptr[qb];
+        int32_t* out = col + bh * p.nnz_per_head + p.row_ptr[qb];
+        if (len >= nB) {                       // dense row
+            for (int kb = lane; kb < nB; kb += 64) out[kb] = kb;
+            continue;
+        }
+        const bool vrow = qb < p.nB_video;
+        const int tq0 = p.blk_tmin[qb], tq1 = p.blk_tmax[qb];
+        uint64_t key[NSLOT];
+        uint64_t fbits = 0;
+        int nforced = 0;
+        uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const int kb = j * 64 + lane;
+            bool forced = false;
+            key[j] = 0;
+            if (kb < nB) {
+                forced = kb >= p.nB_video ||
+                         (vrow && p.same_frame && tq0 <= p.blk_tmax[kb] && p.blk_tmin[kb] <= tq1);
+                if (!forced) {
+                    key[j] = order_key(sc[r * nB + kb]);
+                    kmax = key[j] > kmax ? key[j] : kmax;
+                    kmin = key[j] < kmin ? key[j] : kmin;
+                }
+            }
+            if (forced) fbits |= 1ull << j;
+            nforced += __popcll(__ballot(forced));
+        }
+        const int need = len - nforced;        // blocks to take from the ranking
+        uint64_t T = ~0ull;                    // threshold key (r-th largest)
+        int need_eq = 0;
+        if (need > 0) {
+            kmax = wave_max_u64(kmax);
+            kmin = wave_min_u64(kmin);
+            const uint64_t diff = kmax ^ kmin;
+            int top = diff ? 63 - __clzll(diff) : -1;
+            T = top >= 0 ? (kmin & ~((2ull << top) - 1)) : kmin;
+            if (top == 63) T = 0;
+            // largest T with count(key >= T) >= need
+            for (int bit = top; bit >= 0; --bit) {
+                const uint64_t cand = T | (1ull << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+                if (cnt >= need) T = cand;
+            }
+            int gt = 0;
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) gt += __popcll(__ballot(key[j] > T));
+            need_eq = need - gt;
+        }
+        int base = 0, eq_seen = 0;
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const int kb = j * 64 + lane;
+            const bool forced = (fbits >> j) & 1ull;
+            const bool eq = need > 0 && key[j] == T && kb < nB && !forced;
+            const uint64_t em = __ballot(eq);
+            const int eq_rank = eq_seen + __popcll(em & lt_mask);
+            const bool keep = forced || (need > 0 && key[j] > T) || (eq && eq_rank < need_eq);
+            const uint64_t km = __ballot(keep);
+            const int slot = base + __popcll(km & lt_mask);
+            if (keep && slot < len) out[slot] = kb;
+            base += __popcll(km);
+            eq_seen += __popcll(em);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kr, double* ws,
+                         int32_t* col, hipStream_t s) {
+    const int64_t BH = (int64_t)p.B * p.H;
+    double* qmean = ws;
+    double* kmeanT = ws + BH * p.nB * p.d;
+    {
+        dim3 grid((unsigned)(BH * p.nB), 2);
+        const uint4* q4 = reinterpret_cast<const uint4*>(qr);
+        const uint4* k4 = reinterpret_cast<const uint4*>(kr);
+        if (p.d == 128)
+            hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, s, p, q4, k4, qmean, kmeanT);
+        else
+            hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, s, p, q4, k4, qmean, kmeanT);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    int R = kScoreLds / ((p.nB + p.d) * (int)sizeof(double));
+    R = R < 1 ? 1 : (R > 8 ? 8 : R);
+    const int groups = (p.nB + R - 1) / R;
+    dim3 grid((unsigned)(BH * groups));
+    const size_t lds = (size_t)R * (p.d + p.nB) * sizeof(double);
+    const int nslot = (p.nB + 63) / 64;
+#define SVA_TOPK(DD, NS) \
+    hipLaunchKernelGGL((topk_kernel<DD, NS>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
+    if (p.d == 128) {
+        if (nslot <= 16) SVA_TOPK(128, 16);
+        else if (nslot <= 32) SVA_TOPK(128, 32);
+        else SVA_TOPK(128, 64);
+    } else {
+        if (nslot <= 16) SVA_TOPK(64, 16);
+        else if (nslot <= 32) SVA_TOPK(64, 32);
+        else SVA_TOPK(64, 64);
+    }
+#undef SVA_TOPK
+    return hipGetLastError();
+}
+
+}  // namespace sva

@@ -1,0 +1,61 @@
+// Internal: device view of a plan and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sva {
+
+// Everything a kernel needs to know about a plan, passed by value.
+struct DevPlan {
+    int B, H, d, block;
+    int T, Hh, W;
+    int64_t n_video, N, n_video_pad, Np;
+    int nB, nB_video, k;
+    int dense;          // every block kept
+    int same_frame;     // SVA_KEEP_SAME_FRAME
+    float eps;
+    int rope_off[3];    // offsets (in cos/sin pairs) of the t, h, w tables
+    int rope_half[3];   // rotated pairs per section
+    const float2* rope_cs;
+    const int32_t* perm;       // [N]
+    const int32_t* inv;        // [Np]
+    const int32_t* blk_valid;  // [nB]
+    const int32_t* blk_tmin;   // [nB]
+    const int32_t* blk_tmax;   // [nB]
+    const int32_t* row_ptr;    // [nB+1]
+    int64_t nnz_per_head;
+    int max_row_len;
+};
+
+hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
+                           const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
+                           hipStream_t s);
+
+hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
+                          hipStream_t s);
+
+// ws: [B,H,nB,d] q means followed by [B,H,d,nB] k means (float64)
+hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kr, double* ws,
+                         int32_t* col, hipStream_t s);
+
+hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
+                            const uint16_t* vt, const int32_t* col, uint16_t* o, hipStream_t s);
+
+// ---- small device helpers shared by the kernels ----
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even, hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t v = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+}  // namespace sva

@@ -1,0 +1,266 @@
+// C ABI of the library (declared in include/sva.h): argument checks, plan
+// lifetime and the launch calls.  Every check runs on the host before any
+// work is enqueued; compute calls never synchronise.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "plan_host.h"
+
+namespace sva {
+
+namespace {
+thread_local std::string g_last_error;
+
+int set_err(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_err(hipError_t e, const char* what) {
+    return set_err(SVA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+}  // namespace
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+}  // namespace sva
+
+struct sva_plan_s {
+    sva::HostPlan host;
+    sva::DevPlan dev{};
+    int device = 0;
+    void* dmem = nullptr;   // one allocation holding every device table
+};
+
+using sva::set_err;
+
+extern "C" {
+
+int sva_plan_desc_init(sva_plan_desc* desc, int B, int H, int T, int Hh, int W, int d,
+                       int block, double sparsity, unsigned flags) {
+    if (!desc) return set_err(SVA_ERR_INVALID_ARG, "desc is NULL");
+    std::memset(desc, 0, sizeof(*desc));
+    desc->B = B;
+    desc->H = H;
+    desc->T = T;
+    desc->Hh = Hh;
+    desc->W = W;
+    desc->d = d;
+    desc->block = block;
+    desc->sparsity = sparsity;
+    desc->flags = flags;
+    return SVA_OK;
+}
+
+int sva_plan_query(const sva_plan_desc* desc, sva_plan_info* info) {
+    if (!desc || !info) return set_err(SVA_ERR_INVALID_ARG, "desc or info is NULL");
+    sva::HostPlan hp;
+    std::string err;
+    const int rc = sva::build_host_plan(*desc, hp, err, false);
+    if (rc != SVA_OK) return set_err(rc, err);
+    *info = hp.info;
+    return SVA_OK;
+}
+
+int sva_plan_host_tables(const sva_plan_desc* desc, int32_t* perm, int32_t* row_ptr,
+                         uint8_t* forced) {
+    if (!desc) return set_err(SVA_ERR_INVALID_ARG, "desc is NULL");
+    sva::HostPlan hp;
+    std::string err;
+    const int rc = sva::build_host_plan(*desc, hp, err, false);
+    if (rc != SVA_OK) return set_err(rc, err);
+    if (perm) std::memcpy(perm, hp.perm.data(), hp.perm.size() * sizeof(int32_t));
+    if (row_ptr) std::memcpy(row_ptr, hp.row_ptr.data(), hp.row_ptr.size() * sizeof(int32_t));
+    if (forced) {
+        const int nB = hp.info.nB;
+        for (int qb = 0; qb < nB; ++qb) {
+            const bool dense_row = hp.info.dense || qb >= hp.info.nB_video;
+            for (int kb = 0; kb < nB; ++kb)
+                forced[(size_t)qb * nB + kb] =
+                    (dense_row || sva::forced_pair(hp, qb, kb)) ? 1 : 0;
+        }
+    }
+    return SVA_OK;
+}
+
+int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
+    if (!out || !desc) return set_err(SVA_ERR_INVALID_ARG, "out or desc is NULL");
+    *out = nullptr;
+    sva_plan_s* plan = new (std::nothrow) sva_plan_s();
+    if (!plan) return set_err(SVA_ERR_HIP, "out of host memory");
+    std::string err;
+    int rc = sva::build_host_plan(*desc, plan->host, err, true);
+    if (rc != SVA_OK) {
+        delete plan;
+        return set_err(rc, err);
+    }
+    const sva::HostPlan& h = plan->host;
+    hipError_t e = hipGetDevice(&plan->device);
+    if (e != hipSuccess) {
+        delete plan;
+        return sva::hip_err(e, "hipGetDevice");
+    }
+    // one device buffer: perm, inv, valid, tmin, tmax, row_ptr, rope table
+    auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t s_perm = align(h.perm.size() * 4), s_inv = align(h.inv.size() * 4);
+    const size_t s_blk = align(h.blk_valid.size() * 4), s_rp = align(h.row_ptr.size() * 4);
+    const size_t s_rope = align(h.rope_cs.size() * 4);
+    const size_t total = s_perm + s_inv + 3 * s_blk + s_rp + s_rope;
+    e = hipMalloc(&plan->dmem, total);
+    if (e != hipSuccess) {
+        delete plan;
+        return sva::hip_err(e, "hipMalloc(plan tables)");
+    }
+    char* base = static_cast<char*>(plan->dmem);
+    size_t off = 0;
+    auto put = [&](const void* src, size_t bytes, size_t slot) -> void* {
+        void* dst = base + off;
+        off += slot;
+        if (bytes && e == hipSuccess) e = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
+        return dst;
+    };
+    sva::DevPlan& d = plan->dev;
+    d.perm = static_cast<const int32_t*>(put(h.perm.data(), h.perm.size() * 4, s_perm));
+    d.inv = static_cast<const int32_t*>(put(h.inv.data(), h.inv.size() * 4, s_inv));
+    d.blk_valid = static_cast<const int32_t*>(put(h.blk_valid.data(), h.blk_valid.size() * 4, s_blk));
+    d.blk_tmin = static_cast<const int32_t*>(put(h.blk_tmin.data(), h.blk_tmin.size() * 4, s_blk));
+    d.blk_tmax = static_cast<const int32_t*>(put(h.blk_tmax.data(), h.blk_tmax.size() * 4, s_blk));
+    d.row_ptr = static_cast<const int32_t*>(put(h.row_ptr.data(), h.row_ptr.size() * 4, s_rp));
+    d.rope_cs = static_cast<const float2*>(put(h.rope_cs.data(), h.rope_cs.size() * 4, s_rope));
+    if (e != hipSuccess) {
+        hipFree(plan->dmem);
+        delete plan;
+        return sva::hip_err(e, "hipMemcpy(plan tables)");
+    }
+    const sva_plan_desc& ds = h.desc;
+    const sva_plan_info& I = h.info;
+    d.B = ds.B; d.H = ds.H; d.d = ds.d; d.block = ds.block;
+    d.T = ds.T; d.Hh = ds.Hh; d.W = ds.W;
+    d.n_video = I.n_video; d.N = I.N; d.n_video_pad = I.n_video_pad; d.Np = I.Np;
+    d.nB = I.nB; d.nB_video = I.nB_video; d.k = I.k;
+    d.dense = I.dense;
+    d.same_frame = (ds.flags & SVA_KEEP_SAME_FRAME) ? 1 : 0;
+    d.eps = (float)ds.eps;
+    for (int a = 0; a < 3; ++a) {
+        d.rope_off[a] = h.rope_off[a];
+        d.rope_half[a] = h.rope_half[a];
+    }
+    d.nnz_per_head = I.nnz_per_head;
+    d.max_row_len = I.max_row_len;
+    *out = plan;
+    return SVA_OK;
+}
+
+int sva_plan_create(sva_plan* out, int B, int H, int T, int Hh, int W, int d, int block,
+                    double sparsity, unsigned dense_flag) {
+    sva_plan_desc desc;
+    sva_plan_desc_init(&desc, B, H, T, Hh, W, d, block, sparsity, dense_flag);
+    return sva_plan_create_ex(out, &desc);
+}
+
+int sva_plan_get_info(sva_plan plan, sva_plan_info* info) {
+    if (!plan || !info) return set_err(SVA_ERR_INVALID_ARG, "plan or info is NULL");
+    *info = plan->host.info;
+    return SVA_OK;
+}
+
+int sva_destroy(sva_plan plan) {
+    if (!plan) return SVA_OK;
+    hipError_t e = hipSuccess;
+    if (plan->dmem) e = hipFree(plan->dmem);
+    delete plan;
+    if (e != hipSuccess) return sva::hip_err(e, "hipFree(plan tables)");
+    return SVA_OK;
+}
+
+int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k, const float* wq,
+                     const float* wk, void* q_out, void* k_out, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!q || !k || !q_out || !k_out)
+        return set_err(SVA_ERR_INVALID_ARG, "q, k, q_out and k_out must be non-NULL");
+    if (!sva::aligned16(q) || !sva::aligned16(k) || !sva::aligned16(q_out) ||
+        !sva::aligned16(k_out) || !sva::aligned16(wq) || !sva::aligned16(wk))
+        return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    hipError_t e = sva::launch_prologue(plan->dev, static_cast<const uint16_t*>(q),
+                                        static_cast<const uint16_t*>(k), wq, wk,
+                                        static_cast<uint16_t*>(q_out),
+                                        static_cast<uint16_t*>(k_out),
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "qk_norm_rope launch");
+    return SVA_OK;
+}
+
+int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!in || !out) return set_err(SVA_ERR_INVALID_ARG, "in and out must be non-NULL");
+    if (!sva::aligned16(in) || !sva::aligned16(out))
+        return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (direction != SVA_FORWARD && direction != SVA_INVERSE && direction != SVA_FORWARD_VT)
+        return set_err(SVA_ERR_INVALID_ARG, "unknown reorder direction");
+    if (in == out) return set_err(SVA_ERR_INVALID_ARG, "reorder cannot run in place");
+    hipError_t e = sva::launch_reorder(plan->dev, static_cast<const uint16_t*>(in),
+                                       static_cast<uint16_t*>(out), direction,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "reorder launch");
+    return SVA_OK;
+}
+
+int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r, void* workspace,
+                      size_t workspace_bytes, int32_t* col, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->host.info.dense) return SVA_OK;
+    if (!q_r || !k_r || !col || !workspace)
+        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_r, workspace and col must be non-NULL");
+    if (!sva::aligned16(q_r) || !sva::aligned16(k_r) || !sva::aligned16(workspace) ||
+        ((uintptr_t)col & 3u))
+        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    if (workspace_bytes < plan->host.info.select_workspace_bytes)
+        return set_err(SVA_ERR_WORKSPACE, "workspace smaller than select_workspace_bytes");
+    hipError_t e = sva::launch_select(plan->dev, static_cast<const uint16_t*>(q_r),
+                                      static_cast<const uint16_t*>(k_r),
+                                      static_cast<double*>(workspace), col,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "select launch");
+    return SVA_OK;
+}
+
+int sva_attention(sva_plan plan, const void* q_r, const void* k_r, const void* v_t,
+                  const int32_t* col, void* o_r, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!q_r || !k_r || !v_t || !o_r)
+        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_r, v_t and o_r must be non-NULL");
+    if (!plan->host.info.dense && !col)
+        return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
+    if (!sva::aligned16(q_r) || !sva::aligned16(k_r) || !sva::aligned16(v_t) ||
+        !sva::aligned16(o_r) || ((uintptr_t)col & 3u))
+        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
+                                         static_cast<const uint16_t*>(k_r),
+                                         static_cast<const uint16_t*>(v_t), col,
+                                         static_cast<uint16_t*>(o_r),
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "attention launch");
+    return SVA_OK;
+}
+
+const char* sva_status_string(int status) {
+    switch (status) {
+        case SVA_OK: return "ok";
+        case SVA_ERR_INVALID_ARG: return "invalid argument";
+        case SVA_ERR_UNSUPPORTED: return "unsupported shape";
+        case SVA_ERR_WORKSPACE: return "workspace too small";
+        case SVA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* sva_last_error(void) { return sva::g_last_error.c_str(); }
+
+}  // extern "C"

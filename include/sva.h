@@ -1,0 +1,191 @@
+/*
+ * sva.h — block-sparse video self-attention on MI355X (gfx950).
+ *
+ * One attention call of a video diffusion transformer over T×Hh×W latent
+ * tokens (plus optional extra audio/text tokens), in five steps:
+ *
+ *   sva_qk_norm_rope   QK-RMSNorm + 3D-RoPE on Q and K, fused in one kernel
+ *   sva_reorder        raster tokens -> 3D-tile order (and back for O)
+ *   sva_select_blocks  mean-pooled block scores, top-k key blocks per
+ *                      query block and head
+ *   sva_attention      online-softmax attention over the kept blocks only
+ *
+ * Sources of the operations (web pages on the subject):
+ *  - "MiniMax-H3 在 8×H200 上基准测试" (SGLang Diffusion benchmark),
+ *    section "内核层": QK RMSNorm and 3D RoPE fused in one kernel, with the
+ *    exact rounding path that rounds after the norm, before the rotation;
+ *    section "SubBlock 稀疏注意力如何工作": a pooled score ranks the key
+ *    blocks of each query block and head, the top ones are kept, their
+ *    indices drive a block-sparse attention kernel, the full attention
+ *    matrix is never built; sparsity is the fraction of key blocks dropped;
+ *    the sparse path serves non-causal bf16 attention with head dim 128 and
+ *    falls back to dense attention otherwise.
+ *  - "Sol Video Inference Engine" blog, section 4.2.2: sparse attention
+ *    cuts the quadratic cost of full spatiotemporal attention; Sparse
+ *    VideoGen2 permutes tokens for the GPU layout.
+ *
+ * Conventions
+ *  - All tensors are bf16 (uint16 storage), dense, 16-byte aligned, in
+ *    device memory owned by the caller:
+ *      raster      [B, N, H, d]    token n = (t·Hh + h)·W + w, then extras
+ *      tile order  [B, H, Np, d]   Q, K and O after sva_reorder
+ *      V tiles     [B, H, nB, d, block]   V after SVA_FORWARD_VT: each key
+ *                                  block stored transposed (channel-major)
+ *  - Np = n_video rounded up to a multiple of block, plus n_extra; nB =
+ *    Np / block.  Padding rows of a tile-ordered tensor are zero.
+ *  - Compute calls only enqueue work on `stream` (a hipStream_t; NULL is the
+ *    default stream) and never synchronise.  Argument errors are detected on
+ *    the host before anything is enqueued.  A plan is read-only after
+ *    creation, so it may be used from several streams at once as long as
+ *    each call gets its own output and workspace buffers.
+ *  - Every call returns an SVA_* status; sva_last_error() gives a
+ *    thread-local description of the last failure.
+ */
+#ifndef SVA_H
+#define SVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define SVA_OK               0
+#define SVA_ERR_INVALID_ARG -1  /* bad size, null/misaligned pointer, bad option */
+#define SVA_ERR_UNSUPPORTED -2  /* head dim or block size the kernels do not
+                                   serve (d, block not in {64, 128}); callers
+                                   fall back to dense attention elsewhere */
+#define SVA_ERR_WORKSPACE   -3  /* workspace smaller than required */
+#define SVA_ERR_HIP         -4  /* HIP runtime error (allocation, launch) */
+
+/* ---- plan flags ---- */
+#define SVA_DENSE            1u /* keep every key block (same as sparsity 0):
+                                   the dense warm-up steps of the pages */
+#define SVA_KEEP_SAME_FRAME  2u /* always keep key blocks whose frame range
+                                   meets the query block's frame range */
+
+/* ---- sva_reorder directions ---- */
+#define SVA_FORWARD     0  /* raster [B,N,H,d] -> tile order [B,H,Np,d]      */
+#define SVA_INVERSE     1  /* tile order [B,H,Np,d] -> raster [B,N,H,d]      */
+#define SVA_FORWARD_VT  2  /* raster [B,N,H,d] -> V tiles [B,H,nB,d,block]   */
+
+typedef struct sva_plan_s* sva_plan;
+
+/* Full description of a call.  Fill with sva_plan_desc_init() and change
+ * what differs; zero-valued optional fields take the defaults below. */
+typedef struct {
+    int B, H;             /* batch, heads                                   */
+    int T, Hh, W;         /* latent grid: frames, height, width             */
+    int d;                /* head dim: 64 or 128                            */
+    int block;            /* tokens per block: 64 or 128                    */
+    double sparsity;      /* fraction of key blocks dropped, in [0, 1)      */
+    unsigned flags;       /* SVA_DENSE | SVA_KEEP_SAME_FRAME                */
+    int tile_t, tile_h, tile_w; /* 3D tile; 0,0,0 = 4×4×4 (block 64) or
+                                   2×8×8 (block 128)                        */
+    int n_extra;          /* extra tokens after the video tokens, a multiple
+                             of block; their query rows and key columns are
+                             always dense and they get no RoPE              */
+    double rope_theta;    /* RoPE base; 0 = 10000                           */
+    int rope_split[3];    /* channels for the t, h, w sections, each even;
+                             sum <= d, channels past the sum are not rotated;
+                             0,0,0 = 16/24/24 (d=64) or 44/42/42 (d=128)    */
+    double eps;           /* RMSNorm epsilon; 0 = 1e-6                      */
+} sva_plan_desc;
+
+/* Sizes derived from a description. */
+typedef struct {
+    int64_t n_video;      /* T·Hh·W                                         */
+    int64_t N;            /* n_video + n_extra (raster tokens)              */
+    int64_t n_video_pad;  /* n_video rounded up to a multiple of block      */
+    int64_t Np;           /* n_video_pad + n_extra (tile-ordered rows)      */
+    int32_t nB;           /* Np / block                                     */
+    int32_t nB_video;     /* n_video_pad / block                            */
+    int32_t k;            /* key-block budget per row: ceil((1-sparsity)·nB),
+                             at least 1; nB when dense                      */
+    int32_t max_row_len;  /* longest row of the block list                  */
+    int64_t nnz_per_head; /* kept (query block, key block) pairs per (b, h) */
+    int64_t nnz;          /* B·H·nnz_per_head: length of the col array      */
+    size_t select_workspace_bytes; /* workspace sva_select_blocks needs     */
+    int32_t dense;        /* 1 when every block is kept (no selection)      */
+    int32_t tile[3];      /* resolved tile                                  */
+    int32_t rope_split[3];/* resolved RoPE split                            */
+} sva_plan_info;
+
+/* ---- host-only calls (no device needed) ---- */
+
+/* Fill `desc` with the given shape and defaults for everything else. */
+int sva_plan_desc_init(sva_plan_desc* desc, int B, int H, int T, int Hh, int W,
+                       int d, int block, double sparsity, unsigned flags);
+
+/* Validate `desc` and compute its sizes into `info`. */
+int sva_plan_query(const sva_plan_desc* desc, sva_plan_info* info);
+
+/* Host copies of the plan's fixed tables, each optional (NULL skips it):
+ *   perm     [N]       tile-order position of raster token n
+ *   row_ptr  [nB + 1]  block-list row offsets, shared by every (b, h):
+ *                      row qb of head (b, h) is col[(b·H + h)·nnz_per_head
+ *                      + row_ptr[qb] .. + row_ptr[qb + 1]]
+ *   forced   [nB·nB]   1 where key block kb is always kept for query block
+ *                      qb (extra tokens, same frame); dense rows are all 1 */
+int sva_plan_host_tables(const sva_plan_desc* desc, int32_t* perm,
+                         int32_t* row_ptr, uint8_t* forced);
+
+/* ---- plan lifetime (bound to the current HIP device) ---- */
+
+/* Shape-only plan with default options (see sva_plan_desc_init). */
+int sva_plan_create(sva_plan* out, int B, int H, int T, int Hh, int W, int d,
+                    int block, double sparsity, unsigned dense_flag);
+int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc);
+int sva_plan_get_info(sva_plan plan, sva_plan_info* info);
+/* Frees the plan's device tables.  No work using the plan may be in flight. */
+int sva_destroy(sva_plan plan);
+
+/* ---- compute calls ---- */
+
+/* QK-RMSNorm + 3D-RoPE (fused).  Per (token, head) row x of q and of k:
+ *   y = bf16(x / sqrt(mean(x²) + eps) · w[h])      (norm, rounded first)
+ *   out = bf16(rotate(y))                           (then RoPE, rounded)
+ * where rotate turns channel pairs (2i, 2i+1) of the t, h and w sections by
+ * coordinate · theta^(-2i/width); extra tokens are not rotated.
+ * q, k, q_out, k_out: raster [B, N, H, d] bf16; wq, wk: [H, d] float32 or
+ * NULL for ones.  In place (q_out == q, k_out == k) is allowed. */
+int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k,
+                     const float* wq, const float* wk, void* q_out, void* k_out,
+                     void* stream);
+
+/* Token permutation between raster and 3D-tile order (see direction
+ * macros).  Forward writes zeros into the padding rows; the inverse drops
+ * them.  `in` and `out` must not overlap. */
+int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* stream);
+
+/* Block selection.  q_r, k_r: tile order [B, H, Np, d] (outputs of the
+ * prologue after SVA_FORWARD).  For every (b, h, query block qb):
+ * score(kb) = mean(q_r rows of qb) · mean(k_r rows of kb), means over valid
+ * tokens; keep the forced blocks and then the best-scored blocks (score
+ * descending, lower block index first on equal scores) until the row holds
+ * row_ptr[qb+1] - row_ptr[qb] blocks.  Writes `col` [nnz] int32, each row
+ * in ascending block order.  `workspace` (device, info.select_workspace_bytes)
+ * holds the block means.  Nothing to do for a dense plan (col may be NULL). */
+int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r,
+                      void* workspace, size_t workspace_bytes, int32_t* col,
+                      void* stream);
+
+/* Attention over the kept blocks.  For each valid query row p of block qb:
+ * o_p = sum_j softmax_j(q_p·k_j / sqrt(d)) v_j over the valid keys j of the
+ * blocks in row qb of `col` (any ascending list with the plan's row_ptr is
+ * accepted; a dense plan ignores `col`, which may be NULL).  q_r, k_r:
+ * [B, H, Np, d]; v_t: V tiles [B, H, nB, d, block]; o_r: [B, H, Np, d],
+ * padding rows written as zero. */
+int sva_attention(sva_plan plan, const void* q_r, const void* k_r, const void* v_t,
+                  const int32_t* col, void* o_r, void* stream);
+
+/* ---- errors ---- */
+const char* sva_status_string(int status);
+const char* sva_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVA_H */

@@ -60,7 +60,7 @@ def to_bf16(x):
     _, e = np.frexp(x)
     e = np.maximum(e, -125)
     r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
-    return np.where(np.abs(r) >= 2.0 ** 128, np.sign(x) * np.inf, r)
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
 
 
 def bf16_bits_to_f64(bits):

@@ -1,0 +1,142 @@
+"""Shared helpers of the GPU parity tests (device copies, mask comparison
+with the tie rule, error norms).  Imported by tests only."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import block_sparse_attention_qk_amd as S
+from block_sparse_attention_qk_amd import inputs as I
+import oracle.sva_oracle as O
+
+# Acceptance bar for bf16 outputs against the float64 oracle.
+REL_L2 = 1e-2
+MAX_ABS = 3e-2
+# Relative score margin under which a top-k boundary tie is excused.
+TIE_MARGIN = 1e-6
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bits (host) -> bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 bits on the host."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return O.bf16_bits_to_f64(host(t))
+
+
+def geometry(wl) -> O.Geometry:
+    return O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
+                      sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+
+
+def rel_l2(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_abs(a, ref):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(ref, np.float64))))
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 steps between two arrays of bf16 bit patterns."""
+    def ordered(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def _bf16_step(bits: np.ndarray, delta: int) -> np.ndarray:
+    """bf16 bit patterns moved by `delta` representable steps (through 0)."""
+    u = bits.astype(np.int32)
+    o = np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u) + delta
+    return np.where(o >= 0x8000, o - 0x8000, (0x8000 - o) | 0x8000).astype(np.uint16)
+
+
+def prologue_check(x, w, g, got_bits):
+    """Prologue bar for one (batch, head): x [N, d] float64 inputs, w [d],
+    got_bits [N, d] GPU output.  On the exact-rounding path the output is
+    the rotation of the bf16-rounded norm, so a rounding of the norm that
+    lands on the neighbouring bf16 value moves both outputs of its pair.
+    The bar: every output pair equals, within one bf16 step, the rotation
+    of a normed pair whose elements are each within one bf16 step of the
+    oracle's normed values.  Returns (all_ok, elements differing from the
+    oracle, total elements)."""
+    y = O.to_bf16(O.rms_norm(x, w, g.eps))
+    ref_bits = O.f64_to_bf16_bits(O.rope_3d(y, g))
+    exact = ulp_distance(got_bits, ref_bits)
+    ok = exact <= 1
+    if not ok.all():
+        ybits = O.f64_to_bf16_bits(y)
+        even = np.zeros(y.shape, bool)
+        even[:, 0::2] = True
+        pair_ok = np.zeros((y.shape[0], y.shape[1] // 2), bool)
+        for d0 in (-1, 0, 1):
+            for d1 in (-1, 0, 1):
+                yb = np.where(even, _bf16_step(ybits, d0), _bf16_step(ybits, d1))
+                r = O.f64_to_bf16_bits(O.rope_3d(O.bf16_bits_to_f64(yb), g))
+                e = ulp_distance(got_bits, r) <= 1
+                pair_ok |= e[:, 0::2] & e[:, 1::2]
+        ok = ok | np.repeat(pair_ok, 2, axis=1)
+    return bool(ok.all()), int((exact > 0).sum()), int(exact.size)
+
+
+def kept_from_col(col: np.ndarray, row_ptr: np.ndarray, nB: int) -> np.ndarray:
+    """Kept mask [nB, nB] of one head from its col slice; also checks each
+    row is strictly ascending and in range."""
+    kept = np.zeros((nB, nB), dtype=bool)
+    for qb in range(nB):
+        row = col[row_ptr[qb]: row_ptr[qb + 1]]
+        assert np.all(np.diff(row) > 0), f"row {qb} not strictly ascending"
+        assert row.min() >= 0 and row.max() < nB
+        kept[qb, row] = True
+    return kept
+
+
+def compare_masks(gpu_kept, ref_kept, scores, thresh, smax, forced):
+    """Count mask differences of one head.  A difference on block kb of row
+    qb is excused when kb is not forced and its oracle score lies within
+    TIE_MARGIN·max|score| of the row's last ranked score (a boundary tie:
+    several masks are then correct).  Returns (differences, excused)."""
+    diff = gpu_kept != ref_kept
+    n = int(diff.sum())
+    if n == 0:
+        return 0, 0
+    qb, kb = np.nonzero(diff)
+    ok = (~forced[qb, kb]) & (np.abs(scores[qb, kb] - thresh[qb]) <= TIE_MARGIN * smax[qb])
+    return n, int(ok.sum())
+
+
+class GpuRun:
+    """The whole step on the GPU with every intermediate kept."""
+
+    def __init__(self, wl, q_bits, k_bits, v_bits, wq, wk):
+        self.wl = wl
+        self.plan = S.sva_plan_create_ex(S.desc_for(wl))
+        self.buf = S.Buffers(self.plan)
+        self.q = dev(q_bits)
+        self.k = dev(k_bits)
+        self.v = dev(v_bits)
+        self.wq = torch.from_numpy(np.ascontiguousarray(wq)).cuda()
+        self.wk = torch.from_numpy(np.ascontiguousarray(wk)).cuda()
+
+    def run(self):
+        S.forward(self.plan, self.q, self.k, self.v, self.wq, self.wk, self.buf)
+        torch.cuda.synchronize()
+        return self
+
+
+def workload_inputs(wl):
+    q = I.full_tensor(wl, I.TENSOR_Q)
+    k = I.full_tensor(wl, I.TENSOR_K)
+    v = I.full_tensor(wl, I.TENSOR_V)
+    wq, wk = I.norm_weights(wl)
+    return q, k, v, wq, wk

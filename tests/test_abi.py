@@ -1,0 +1,114 @@
+"""CPU tests of the C ABI: the library loads, exports every declared
+symbol, and its host-side planning (sizes, permutation, block budget, row
+offsets, forced blocks, argument errors) equals the oracle's bit for bit.
+No compute call runs here (no GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_qk_amd as S
+from block_sparse_attention_qk_amd import inputs as I
+import oracle.sva_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "sva.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(sva_\w+)\s*\(", header, re.M))
+    assert declared == set(S.EXPORTED)
+    L = S.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert S.sva_status_string(S.SVA_ERR_WORKSPACE) == "workspace too small"
+
+
+def _geom(wl):
+    return O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
+                      sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+
+
+CASES = list(I.WORKLOADS.values()) + [
+    I.custom("ragged", 2, 3, 5, 13, 17, 128, 128, 0.6, flags=I.KEEP_SAME_FRAME,
+             n_extra=128),
+    I.custom("ragged64", 1, 2, 3, 7, 11, 64, 64, 0.5, tile=(2, 3, 4), n_extra=64),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_host_plan_equals_oracle(wl):
+    g = _geom(wl)
+    info = S.sva_plan_query(S.desc_for(wl))
+    assert (info.n_video, info.N, info.n_video_pad, info.Np) == (g.n_video, g.N, g.n_video_pad, g.Np)
+    assert (info.nB, info.nB_video, info.k) == (g.nB, g.nB_video, g.k)
+    assert bool(info.dense) == g.dense
+    perm, row_ptr, forced = S.sva_plan_host_tables(S.desc_for(wl), forced=g.nB <= 1024)
+    assert np.array_equal(perm, O.permutation(g))
+    lens = O.row_lengths(g)
+    assert np.array_equal(np.diff(row_ptr), lens)
+    assert info.nnz_per_head == lens.sum() and info.nnz == lens.sum() * wl.B * wl.H
+    assert info.max_row_len == lens.max()
+    if forced is not None:
+        f_o, dense_row = O.forced_blocks(g)
+        want = f_o | dense_row[:, None]
+        assert np.array_equal(forced.astype(bool), want)
+
+
+def test_workload_block_lists():
+    """The executed block pairs of the bench workload (75,600 tokens,
+    128-token blocks, sparsity 0.75): 591 rows of 148 blocks per head."""
+    info = S.sva_plan_query(S.desc_for(I.WORKLOADS["wan720p_sp75"]))
+    assert (info.nB, info.k, info.max_row_len, info.nnz_per_head) == (591, 148, 148, 591 * 148)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), S.SVA_ERR_UNSUPPORTED),
+    (dict(block=32), S.SVA_ERR_UNSUPPORTED),
+    (dict(B=0), S.SVA_ERR_INVALID_ARG),
+    (dict(T=-1), S.SVA_ERR_INVALID_ARG),
+    (dict(sparsity=1.0), S.SVA_ERR_INVALID_ARG),
+    (dict(sparsity=-0.1), S.SVA_ERR_INVALID_ARG),
+    (dict(sparsity=float("nan")), S.SVA_ERR_INVALID_ARG),
+    (dict(flags=8), S.SVA_ERR_INVALID_ARG),
+    (dict(n_extra=100), S.SVA_ERR_INVALID_ARG),
+    (dict(tile=(0, 4, 4)), S.SVA_ERR_INVALID_ARG),
+    (dict(rope_split=(43, 43, 42)), S.SVA_ERR_INVALID_ARG),
+    (dict(rope_split=(64, 64, 64)), S.SVA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), S.SVA_ERR_INVALID_ARG),
+    (dict(rope_theta=0.5), S.SVA_ERR_INVALID_ARG),
+])
+def test_argument_errors(kw, status):
+    base = dict(B=1, H=2, T=4, Hh=8, W=8, d=128, block=128, sparsity=0.5)
+    extra = {k: kw.pop(k) for k in list(kw) if k in ("tile", "n_extra", "rope_split", "eps",
+                                                     "rope_theta", "flags")}
+    base.update(kw)
+    desc = S.sva_plan_desc_init(base["B"], base["H"], base["T"], base["Hh"], base["W"],
+                                base["d"], base["block"], base["sparsity"],
+                                extra.pop("flags", 0), **extra)
+    with pytest.raises(S.SvaError) as e:
+        S.sva_plan_query(desc)
+    assert e.value.status == status
+    assert S.sva_last_error()
+
+
+def test_null_arguments_rejected_on_host():
+    L = S.lib()
+    assert L.sva_plan_query(None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_plan_get_info(None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_qk_norm_rope(None, None, None, None, None, None, None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_reorder(None, None, None, 0, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_select_blocks(None, None, None, None, 0, None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_attention(None, None, None, None, None, None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_destroy(None) == S.SVA_OK
+    assert L.sva_plan_create_ex(None, None) == S.SVA_ERR_INVALID_ARG
+
+
+def test_partial_rope_split_accepted():
+    # 96 of 128 channels rotated (the packed H3 shape on the benchmark page)
+    desc = S.sva_plan_desc_init(1, 2, 4, 8, 8, 128, 128, 0.5, rope_split=(32, 32, 32))
+    info = S.sva_plan_query(desc)
+    assert list(info.rope_split) == [32, 32, 32]

@@ -1,0 +1,337 @@
+"""GPU parity of every step against the float64 oracle, through the C ABI.
+
+Stage tests feed the GPU and the oracle identical inputs; the chained
+tests run the whole step from the raw inputs on both sides.  Bars:
+  - reorder: bit-exact;
+  - block mask: bit-exact except top-k boundary ties (oracle score within
+    1e-6·max|score| of the row's cut), which are counted;
+  - prologue: each output pair within one bf16 step of the rotation of a
+    normed pair that is itself within one bf16 step of the oracle's normed
+    values (the exact-rounding path rounds before rotating, so a norm
+    rounding that lands on the neighbouring value moves its pair), and at
+    most 1e-3 of the elements differing from the oracle at all;
+  - attention output (bf16): relative L2 <= 1e-2 and max abs <= 3e-2.
+Small shapes are checked completely; the named workloads at full size are
+checked on sampled heads and query blocks (the launch configuration is the
+one the benchmark times).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_qk_amd as S
+from block_sparse_attention_qk_amd import inputs as I
+import oracle.sva_oracle as O
+from _parity import (MAX_ABS, REL_L2, GpuRun, compare_masks, dev, geometry, host, host_f64,
+                     kept_from_col, max_abs, prologue_check, rel_l2, workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": I.WORKLOADS["tiny"],
+    "ragged128": I.custom("ragged128", 2, 3, 5, 13, 17, 128, 128, 0.6,
+                          flags=I.KEEP_SAME_FRAME, n_extra=128, temperature=True,
+                          seed_base=9100),
+    "ragged64": I.custom("ragged64", 1, 2, 6, 10, 14, 64, 64, 0.5, tile=(2, 3, 4),
+                         n_extra=64, seed_base=9200),
+    "d128_b64": I.custom("d128_b64", 1, 2, 4, 12, 20, 128, 64, 0.7, tile=(4, 4, 4),
+                         seed_base=9300),
+    "d64_b128": I.custom("d64_b128", 1, 2, 4, 12, 20, 64, 128, 0.5, tile=(2, 8, 8),
+                         n_extra=128, flags=I.KEEP_SAME_FRAME, seed_base=9400),
+    "dense128": I.custom("dense128", 1, 2, 5, 13, 17, 128, 128, 0.0, seed_base=9500),
+    "denseflag64": I.custom("denseflag64", 1, 2, 3, 9, 20, 64, 64, 0.8, flags=I.DENSE,
+                            tile=(1, 4, 16), seed_base=9600),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+_cache = {}
+
+
+def small_case(name):
+    if name not in _cache:
+        wl = SMALL[name]
+        q, k, v, wq, wk = workload_inputs(wl)
+        g = geometry(wl)
+        perm = O.permutation(g)
+        meta = O.block_meta(g, perm)
+        ref = {}
+        for b in range(wl.B):
+            for h in range(wl.H):
+                ref[b, h] = O.run_head(O.bf16_bits_to_f64(q[b, :, h]), O.bf16_bits_to_f64(k[b, :, h]),
+                                       O.bf16_bits_to_f64(v[b, :, h]), wq[h], wk[h], g,
+                                       perm=perm, meta=meta)
+        _cache[name] = (wl, g, perm, meta, (q, k, v, wq, wk), ref)
+    return _cache[name]
+
+
+def _vt_from_vr(vr_bits, g):
+    """[Np, d] tile-ordered rows -> [nB, d, block] transposed blocks."""
+    return np.ascontiguousarray(vr_bits.reshape(g.nB, g.block, g.d).transpose(0, 2, 1))
+
+
+def _vr_from_vt(vt_bits, g):
+    return np.ascontiguousarray(vt_bits.transpose(0, 2, 1).reshape(g.Np, g.d))
+
+
+def _col_from_kept(kept_per_bh, g, B, H):
+    cols = []
+    for b in range(B):
+        for h in range(H):
+            cols.append(np.nonzero(kept_per_bh[b, h])[1])
+    return np.concatenate(cols).astype(np.int32)
+
+
+# ------------------------------------------------------------------ stage tests
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prologue_parity(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    S.sva_qk_norm_rope(run.plan, run.q, run.k, run.wq, run.wk, run.buf.qn, run.buf.kn)
+    torch.cuda.synchronize()
+    qn, kn = host(run.buf.qn), host(run.buf.kn)
+    mism = total = 0
+    for (b, h) in ref:
+        for got, x, w in ((qn[b, :, h], q[b, :, h], wq[h]), (kn[b, :, h], k[b, :, h], wk[h])):
+            ok, n, t = prologue_check(O.bf16_bits_to_f64(x), w, g, got)
+            assert ok, (b, h)
+            mism += n
+            total += t
+    print(f"{name}: prologue elements differing from the oracle: {mism}/{total}")
+    assert mism <= 1e-3 * total
+    # in place gives the same bits
+    S.sva_qk_norm_rope(run.plan, run.q, run.k, run.wq, run.wk, run.q, run.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(run.q), qn) and np.array_equal(host(run.k), kn)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_reorder_parity(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    S.sva_reorder(run.plan, run.q, run.buf.q_r, S.SVA_FORWARD)
+    S.sva_reorder(run.plan, run.v, run.buf.v_t, S.SVA_FORWARD_VT)
+    torch.cuda.synchronize()
+    want = O.reorder_forward(q, g, perm)                      # uint16 bits move as-is
+    assert np.array_equal(host(run.buf.q_r), want)
+    wv = O.reorder_forward(v, g, perm)
+    vt = host(run.buf.v_t)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            assert np.array_equal(vt[b, h], _vt_from_vr(wv[b, h], g))
+    # inverse of the forward returns the input; the padding rows are dropped
+    S.sva_reorder(run.plan, run.buf.q_r, run.buf.o, S.SVA_INVERSE)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(run.buf.o), q)
+
+
+@pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].sparsity > 0
+                                  and not SMALL[n].flags & I.DENSE])
+def test_select_parity(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    qr = np.zeros((wl.B, wl.H, g.Np, g.d), np.uint16)
+    kr = np.zeros_like(qr)
+    for (b, h), r in ref.items():
+        qr[b, h] = O.f64_to_bf16_bits(r["qr"])
+        kr[b, h] = O.f64_to_bf16_bits(r["kr"])
+    S.sva_select_blocks(run.plan, dev(qr), dev(kr), run.buf.ws, run.buf.col)
+    torch.cuda.synchronize()
+    col = run.buf.col.cpu().numpy()
+    _, row_ptr, _ = run.plan.host_tables()
+    forced, dense_row = O.forced_blocks(g, meta)
+    nnz = int(run.plan.info.nnz_per_head)
+    diffs = excused = 0
+    for (b, h), r in ref.items():
+        bh = b * wl.H + h
+        kept = kept_from_col(col[bh * nnz:(bh + 1) * nnz], row_ptr, g.nB)
+        n, e = compare_masks(kept, r["kept"], r["scores"], r["thresh"], r["smax"], forced)
+        diffs += n
+        excused += e
+    print(f"{name}: mask differences {diffs}, excused ties {excused}")
+    assert diffs == excused
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attention_parity(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    B, H = wl.B, wl.H
+    qr = np.zeros((B, H, g.Np, g.d), np.uint16)
+    kr = np.zeros_like(qr)
+    vt = np.zeros((B, H, g.nB, g.d, g.block), np.uint16)
+    kept = np.zeros((B, H, g.nB, g.nB), bool)
+    for (b, h), r in ref.items():
+        qr[b, h] = O.f64_to_bf16_bits(r["qr"])
+        kr[b, h] = O.f64_to_bf16_bits(r["kr"])
+        vt[b, h] = _vt_from_vr(O.f64_to_bf16_bits(r["vr"]), g)
+        kept[b, h] = r["kept"]
+    col = None if run.plan.info.dense else dev_col(_col_from_kept(kept, g, B, H))
+    S.sva_attention(run.plan, dev(qr), dev(kr), dev(vt), col, run.buf.o_r)
+    torch.cuda.synchronize()
+    out = host_f64(run.buf.o_r)
+    worst_rel, worst_abs = 0.0, 0.0
+    for (b, h), r in ref.items():
+        worst_rel = max(worst_rel, rel_l2(out[b, h], r["o_r"]))
+        worst_abs = max(worst_abs, max_abs(out[b, h], r["o_r"]))
+        pad = np.ones(g.Np, bool)
+        for blk in range(g.nB):
+            pad[blk * g.block: blk * g.block + meta[0][blk]] = False
+        assert np.all(out[b, h][pad] == 0)
+    print(f"{name}: attention rel_l2 {worst_rel:.2e} max_abs {worst_abs:.2e}")
+    assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
+
+
+def dev_col(col_np):
+    return torch.from_numpy(col_np).cuda()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_chained_parity(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk).run()
+    out = host_f64(run.buf.o)
+    worst_rel, worst_abs = 0.0, 0.0
+    for (b, h), r in ref.items():
+        worst_rel = max(worst_rel, rel_l2(out[b, :, h], r["o"]))
+        worst_abs = max(worst_abs, max_abs(out[b, :, h], r["o"]))
+    diffs = 0
+    if not run.plan.info.dense:
+        col = run.buf.col.cpu().numpy()
+        _, row_ptr, _ = run.plan.host_tables()
+        nnz = int(run.plan.info.nnz_per_head)
+        for (b, h), r in ref.items():
+            bh = b * wl.H + h
+            kept = kept_from_col(col[bh * nnz:(bh + 1) * nnz], row_ptr, g.nB)
+            diffs += int((kept != r["kept"]).sum())
+    print(f"{name}: chained rel_l2 {worst_rel:.2e} max_abs {worst_abs:.2e} mask diffs {diffs}")
+    assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
+
+
+@pytest.mark.parametrize("name", ["ragged128", "tiny"])
+def test_deterministic(name):
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk).run()
+    a = host(run.buf.o).copy()
+    ca = run.buf.col.cpu().numpy().copy() if run.buf.col is not None else None
+    run.run()
+    assert np.array_equal(host(run.buf.o), a)
+    if ca is not None:
+        assert np.array_equal(run.buf.col.cpu().numpy(), ca)
+
+
+def test_binding_rejects_bad_tensors():
+    wl = SMALL["tiny"]
+    plan = S.sva_plan_create_ex(S.desc_for(wl))
+    buf = S.Buffers(plan)
+    bad = torch.zeros(plan.raster_shape, dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        S.sva_reorder(plan, bad, buf.q_r, S.SVA_FORWARD)
+    with pytest.raises(ValueError):
+        S.sva_reorder(plan, buf.qn[:, :-1], buf.q_r, S.SVA_FORWARD)
+    with pytest.raises(ValueError):
+        S.sva_reorder(plan, buf.qn.cpu(), buf.q_r, S.SVA_FORWARD)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(S.SvaError) as e:
+        S.sva_select_blocks(plan, buf.q_r, buf.k_r, small_ws, buf.col)
+    assert e.value.status == S.SVA_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+FULL = ["wan480p_dense", "wan480p_sp75", "wan720p_sp75", "hunyuan720p_sp80",
+        "hunyuan720p_dense", "packed768p_sp80"]
+_full_cache = {}
+
+
+def _full_inputs(wl):
+    key = wl.seed_base
+    if key not in _full_cache:
+        _full_cache.clear()
+        _full_cache[key] = workload_inputs(wl)
+    return _full_cache[key]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled(name):
+    wl = I.WORKLOADS[name]
+    g = geometry(wl)
+    q, k, v, wq, wk = _full_inputs(wl)
+    print(f"{name}: inputs ready", flush=True)
+    run = GpuRun(wl, q, k, v, wq, wk).run()
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    forced, dense_row = O.forced_blocks(g, meta)
+    rng = np.random.default_rng(wl.seed_base + 7)
+    heads = sorted({0, wl.H - 1, int(rng.integers(0, wl.H))})
+    qbs = sorted({0, g.nB_video - 1, g.nB - 1, *rng.integers(0, g.nB, 5).tolist()})
+    _, row_ptr, _ = run.plan.host_tables()
+    nnz = int(run.plan.info.nnz_per_head)
+    col = run.buf.col.cpu().numpy() if run.buf.col is not None else None
+    stats = dict(ulp_mism=0, elems=0, mask_diffs=0, mask_excused=0, chain_mask_diffs=0)
+    worst = dict(att_rel=0.0, att_abs=0.0, ch_rel=0.0, ch_abs=0.0)
+    for h in heads:
+        qh = O.bf16_bits_to_f64(q[0, :, h])
+        kh = O.bf16_bits_to_f64(k[0, :, h])
+        vh = O.bf16_bits_to_f64(v[0, :, h])
+        # prologue
+        qn_g = host(run.buf.qn[0, :, h])
+        kn_g = host(run.buf.kn[0, :, h])
+        for got, x, w in ((qn_g, qh, wq[h]), (kn_g, kh, wk[h])):
+            ok, n, t = prologue_check(x, w, g, got)
+            assert ok, h
+            stats["ulp_mism"] += n
+            stats["elems"] += t
+        # reorder (bit-exact, from the GPU's own prologue output)
+        qr_g = host(run.buf.q_r[0, h])
+        kr_g = host(run.buf.k_r[0, h])
+        vt_g = host(run.buf.v_t[0, h])
+        want = np.zeros((g.Np, g.d), np.uint16)
+        want[perm] = qn_g
+        assert np.array_equal(qr_g, want)
+        want[perm] = kn_g
+        assert np.array_equal(kr_g, want)
+        want[perm] = v[0, :, h]
+        assert np.array_equal(vt_g, _vt_from_vr(want, g))
+        vr_f = O.bf16_bits_to_f64(want)
+        # selection on the GPU's own tile-ordered Q', K' (identical inputs)
+        qr_f = O.bf16_bits_to_f64(qr_g)
+        kr_f = O.bf16_bits_to_f64(kr_g)
+        if col is not None:
+            kept_ref, scores, thresh, smax = O.select_blocks(
+                O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]), g, meta)
+            kept_g = kept_from_col(col[h * nnz:(h + 1) * nnz], row_ptr, g.nB)
+            n, e = compare_masks(kept_g, kept_ref, scores, thresh, smax, forced)
+            stats["mask_diffs"] += n
+            stats["mask_excused"] += e
+        else:
+            kept_g = np.ones((g.nB, g.nB), bool)
+        # attention on identical inputs and the GPU's block list
+        o_ref = O.block_attention(qr_f, kr_f, vr_f, kept_g, g, meta, qblocks=qbs)
+        o_g = host_f64(run.buf.o_r[0, h])
+        rows = np.concatenate([np.arange(b * g.block, (b + 1) * g.block) for b in qbs])
+        worst["att_rel"] = max(worst["att_rel"], rel_l2(o_g[rows], o_ref[rows]))
+        worst["att_abs"] = max(worst["att_abs"], max_abs(o_g[rows], o_ref[rows]))
+        # inverse reorder of O (bit-exact)
+        o_rast = host(run.buf.o[0, :, h])
+        assert np.array_equal(o_rast, host(run.buf.o_r[0, h])[perm])
+        # chained: the oracle from the raw inputs
+        r = O.run_head(qh, kh, vh, wq[h], wk[h], g, qblocks=qbs, perm=perm, meta=meta)
+        stats["chain_mask_diffs"] += int((r["kept"] != kept_g).sum())
+        worst["ch_rel"] = max(worst["ch_rel"], rel_l2(o_g[rows], r["o_r"][rows]))
+        worst["ch_abs"] = max(worst["ch_abs"], max_abs(o_g[rows], r["o_r"][rows]))
+    print(f"{name}: heads {heads} qblocks {qbs} {stats} {worst}", flush=True)
+    assert stats["ulp_mism"] <= 1e-3 * stats["elems"]
+    assert stats["mask_diffs"] == stats["mask_excused"]
+    assert worst["att_rel"] <= REL_L2 and worst["att_abs"] <= MAX_ABS
+    assert worst["ch_rel"] <= REL_L2 and worst["ch_abs"] <= MAX_ABS
