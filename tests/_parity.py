@@ -61,31 +61,48 @@ def _bf16_step(bits: np.ndarray, delta: int) -> np.ndarray:
     return np.where(o >= 0x8000, o - 0x8000, (0x8000 - o) | 0x8000).astype(np.uint16)
 
 
-def prologue_check(x, w, g, got_bits):
+def prologue_check(x, w, g, got_bits, report=None):
     """Prologue bar for one (batch, head): x [N, d] float64 inputs, w [d],
-    got_bits [N, d] GPU output.  On the exact-rounding path the output is
-    the rotation of the bf16-rounded norm, so a rounding of the norm that
-    lands on the neighbouring bf16 value moves both outputs of its pair.
-    The bar: every output pair equals, within one bf16 step, the rotation
-    of a normed pair whose elements are each within one bf16 step of the
-    oracle's normed values.  Returns (all_ok, elements differing from the
-    oracle, total elements)."""
+    got_bits [N, d] GPU output.
+
+    The exact-rounding path rounds the norm to bf16 and rotates that, so
+    (a) a norm rounding that lands on the neighbouring bf16 value moves
+    both outputs of its pair, and (b) the rotation, evaluated in float32
+    with float32 cos/sin (each within 2^-24 relative) and two roundings,
+    is off by at most a few 2^-24·(|y0| + |y1|) before its own rounding,
+    which is many bf16 steps of the output when y0·c - y1·s nearly cancels.
+    The bar: every output pair is within one bf16 step plus
+    2^-21·(|y0'| + |y1'|) of the rotation of a normed pair (y0', y1') whose
+    elements are each within one bf16 step of the oracle's.  Returns
+    (all_ok, elements differing from the oracle, total elements)."""
     y = O.to_bf16(O.rms_norm(x, w, g.eps))
     ref_bits = O.f64_to_bf16_bits(O.rope_3d(y, g))
     exact = ulp_distance(got_bits, ref_bits)
     ok = exact <= 1
     if not ok.all():
+        got = O.bf16_bits_to_f64(got_bits)
         ybits = O.f64_to_bf16_bits(y)
         even = np.zeros(y.shape, bool)
         even[:, 0::2] = True
         pair_ok = np.zeros((y.shape[0], y.shape[1] // 2), bool)
         for d0 in (-1, 0, 1):
             for d1 in (-1, 0, 1):
-                yb = np.where(even, _bf16_step(ybits, d0), _bf16_step(ybits, d1))
-                r = O.f64_to_bf16_bits(O.rope_3d(O.bf16_bits_to_f64(yb), g))
-                e = ulp_distance(got_bits, r) <= 1
+                yb = O.bf16_bits_to_f64(np.where(even, _bf16_step(ybits, d0),
+                                                 _bf16_step(ybits, d1)))
+                rot = O.rope_3d(yb, g)
+                mag = np.repeat(np.abs(yb[:, 0::2]) + np.abs(yb[:, 1::2]), 2, axis=1)
+                step = np.abs(O.bf16_bits_to_f64(_bf16_step(O.f64_to_bf16_bits(rot), 1))
+                              - O.to_bf16(rot))
+                e = np.abs(got - rot) <= step + 2.0 ** -21 * mag
                 pair_ok |= e[:, 0::2] & e[:, 1::2]
         ok = ok | np.repeat(pair_ok, 2, axis=1)
+        if report is not None and not ok.all():
+            bad = np.argwhere(~ok)[:5]
+            for n, c in bad:
+                report.append(dict(token=int(n), ch=int(c), gpu=float(got[n, c]),
+                                   oracle=float(O.bf16_bits_to_f64(ref_bits[n, c])),
+                                   y=y[n, (c // 2) * 2:(c // 2) * 2 + 2].tolist(),
+                                   x=x[n, (c // 2) * 2:(c // 2) * 2 + 2].tolist()))
     return bool(ok.all()), int((exact > 0).sum()), int(exact.size)
 
 

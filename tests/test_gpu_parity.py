@@ -101,8 +101,9 @@ def test_prologue_parity(name):
     mism = total = 0
     for (b, h) in ref:
         for got, x, w in ((qn[b, :, h], q[b, :, h], wq[h]), (kn[b, :, h], k[b, :, h], wk[h])):
-            ok, n, t = prologue_check(O.bf16_bits_to_f64(x), w, g, got)
-            assert ok, (b, h)
+            rep = []
+            ok, n, t = prologue_check(O.bf16_bits_to_f64(x), w, g, got, rep)
+            assert ok, ((b, h), rep)
             mism += n
             total += t
     print(f"{name}: prologue elements differing from the oracle: {mism}/{total}")
@@ -279,8 +280,10 @@ def test_full_workload_sampled(name):
     nnz = int(run.plan.info.nnz_per_head)
     col = run.buf.col.cpu().numpy() if run.buf.col is not None else None
     stats = dict(ulp_mism=0, elems=0, mask_diffs=0, mask_excused=0, chain_mask_diffs=0)
+    fails = []
     worst = dict(att_rel=0.0, att_abs=0.0, ch_rel=0.0, ch_abs=0.0)
     for h in heads:
+        print(f"{name}: checking head {h}", flush=True)
         qh = O.bf16_bits_to_f64(q[0, :, h])
         kh = O.bf16_bits_to_f64(k[0, :, h])
         vh = O.bf16_bits_to_f64(v[0, :, h])
@@ -288,8 +291,10 @@ def test_full_workload_sampled(name):
         qn_g = host(run.buf.qn[0, :, h])
         kn_g = host(run.buf.kn[0, :, h])
         for got, x, w in ((qn_g, qh, wq[h]), (kn_g, kh, wk[h])):
-            ok, n, t = prologue_check(x, w, g, got)
-            assert ok, h
+            rep = []
+            ok, n, t = prologue_check(x, w, g, got, rep)
+            if not ok:
+                fails.append(("prologue", h, rep))
             stats["ulp_mism"] += n
             stats["elems"] += t
         # reorder (bit-exact, from the GPU's own prologue output)
@@ -298,11 +303,14 @@ def test_full_workload_sampled(name):
         vt_g = host(run.buf.v_t[0, h])
         want = np.zeros((g.Np, g.d), np.uint16)
         want[perm] = qn_g
-        assert np.array_equal(qr_g, want)
+        if not np.array_equal(qr_g, want):
+            fails.append(("reorder q", h))
         want[perm] = kn_g
-        assert np.array_equal(kr_g, want)
+        if not np.array_equal(kr_g, want):
+            fails.append(("reorder k", h))
         want[perm] = v[0, :, h]
-        assert np.array_equal(vt_g, _vt_from_vr(want, g))
+        if not np.array_equal(vt_g, _vt_from_vr(want, g)):
+            fails.append(("reorder v tiles", h))
         vr_f = O.bf16_bits_to_f64(want)
         # selection on the GPU's own tile-ordered Q', K' (identical inputs)
         qr_f = O.bf16_bits_to_f64(qr_g)
@@ -324,13 +332,15 @@ def test_full_workload_sampled(name):
         worst["att_abs"] = max(worst["att_abs"], max_abs(o_g[rows], o_ref[rows]))
         # inverse reorder of O (bit-exact)
         o_rast = host(run.buf.o[0, :, h])
-        assert np.array_equal(o_rast, host(run.buf.o_r[0, h])[perm])
+        if not np.array_equal(o_rast, host(run.buf.o_r[0, h])[perm]):
+            fails.append(("reorder inverse", h))
         # chained: the oracle from the raw inputs
         r = O.run_head(qh, kh, vh, wq[h], wk[h], g, qblocks=qbs, perm=perm, meta=meta)
         stats["chain_mask_diffs"] += int((r["kept"] != kept_g).sum())
         worst["ch_rel"] = max(worst["ch_rel"], rel_l2(o_g[rows], r["o_r"][rows]))
         worst["ch_abs"] = max(worst["ch_abs"], max_abs(o_g[rows], r["o_r"][rows]))
     print(f"{name}: heads {heads} qblocks {qbs} {stats} {worst}", flush=True)
+    assert not fails, fails
     assert stats["ulp_mism"] <= 1e-3 * stats["elems"]
     assert stats["mask_diffs"] == stats["mask_excused"]
     assert worst["att_rel"] <= REL_L2 and worst["att_abs"] <= MAX_ABS
