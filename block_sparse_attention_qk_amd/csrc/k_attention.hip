@@ -8,22 +8,32 @@
 // when m grows.  A dense plan walks every block and is exact dense
 // attention ("SVA_DENSE", the dense warm-up steps of the same page).
 //
-// Work split: one workgroup per (b, h, qb); one wave per 32 query rows
-// (BLK/32 waves).  Per key block the workgroup stages K (row-major) and V
-// (transposed tile, as written by the V-tile reorder) in LDS, then each
+// Work split: one workgroup per (b, h, qb), one wave per 32 query rows
+// (BLK/32 waves), two workgroups per CU (64 KB of LDS and <= 256 registers
+// per wave each), so every SIMD holds two waves whose MFMA and softmax
+// phases interleave.  A row's key blocks are consumed in stages of 64
+// keys; the workgroup keeps two LDS stage buffers and issues the global
+// loads of stage s+1 into registers before computing stage s, writing them
+// to the other buffer afterwards (one barrier per stage).  Per stage each
 // wave computes
 //   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries
 //   softmax on S^T   each lane owns one query column: row max and sums are
 //                    lane-local plus one exchange between the two lane halves
 //   O^T += V^T · P^T v_mfma_f32_32x32x16_bf16, M = channels, N = queries;
-//                    P^T comes straight from the S^T accumulators, with the
-//                    contraction order of the keys matched on the V side.
-// Logits are scaled by log2(e)/sqrt(d) and exponentiated with exp2.
+//                    P^T comes straight from the S^T accumulators; the V
+//                    tiles store keys in the order that accumulator layout
+//                    hands them over (see the V-tile reorder), so each V
+//                    operand is one 16-byte LDS read.
+// Logits are scaled by log2(e)/sqrt(d) and exponentiated with v_exp_f32.
+// The running max is raised only when a row's new max exceeds it by more
+// than 8 (log2 units); in between, probabilities are taken against the
+// stale max (at most 2^8, exact in the final division), which skips most
+// rescales of the accumulator.
 //
-// LDS layouts avoid bank conflicts with XOR swizzles: K rows (keys) of d
-// bf16 in 16-byte chunks, chunk c of row r at c ^ (r mod 16); V^T rows
-// (channels) of BLK keys in 8-byte units, unit u of row r at u ^ (r mod
-// BLK/4).  Each lane of an MFMA operand read then hits its own banks.
+// LDS layouts avoid bank conflicts with XOR swizzles of 16-byte chunks: a
+// row of 256 bytes puts chunk c at c ^ (r mod 16), a row of 128 bytes at
+// c ^ ((r/2) mod 8), so the 16 lanes served together read 16 different bank
+// groups.
 //
 // Roofline: 4·BLK²·d flops per (query block, key block) pair on the MFMA
 // pipe (8.4 MFLOP at BLK = d = 128) against 2·BLK·d·2 bytes of K and V
@@ -37,17 +47,18 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
     DevPlan p;
-    const uint4* q;      // [B,H,Np,d]
-    const uint4* k;      // [B,H,Np,d]
-    const uint4* vt;     // [B,H,nB,d,BLK]
+    const u32x4_t* q;    // [B,H,Np,d]
+    const u32x4_t* k;    // [B,H,Np,d]
+    const u32x4_t* vt;   // [B,H,nB,d,BLK]
     const int32_t* col;  // [B,H,nnz_per_head]
     uint2* o;            // [B,H,Np,d]
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ float lane_swap_max(float x) {
     // v_permlane32_swap: both outputs hold {x[l mod 32], x[l mod 32 + 32]}
@@ -71,16 +82,29 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t n) {
     return x * per + (x < rem ? x : rem) + idx;
 }
 
+// 16-byte chunk slot of chunk c in LDS row r (rows of RB bytes).
+template <int RB>
+__device__ __forceinline__ int swz(int c, int r) {
+    if constexpr (RB == 256) return c ^ (r & 15);
+    else return c ^ ((r >> 1) & 7);
+}
+
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnArgs a) {
-    constexpr int NT = BLK * 2;        // threads (BLK/32 waves)
-    constexpr int KCH = D / 8;         // 16-byte chunks per K row
-    constexpr int VU = BLK / 4;        // 8-byte units per V^T row
-    constexpr int KT = BLK / 32;       // 32-key tiles per block
-    constexpr int DS = D / 16;         // 16-channel steps (S^T contraction)
-    constexpr int DT = D / 32;         // 32-channel tiles (O^T rows)
-    __shared__ uint4 sK[BLK * KCH];
-    __shared__ uint2 sV[D * VU];
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_kernel(AttnArgs a) {
+    constexpr int NT = BLK * 2;          // threads (BLK/32 waves)
+    constexpr int SK = 64;               // keys per stage
+    constexpr int SPB = BLK / SK;        // stages per block
+    constexpr int KCH = D / 8;           // 16-byte chunks per K row
+    constexpr int KRB = D * 2;           // bytes per K row
+    constexpr int VCH = SK / 8;          // 16-byte chunks per V^T stage row
+    constexpr int KPT = SK * KCH / NT;   // K chunks per thread per stage
+    constexpr int VPT = D * VCH / NT;    // V chunks per thread per stage
+    constexpr int DS = D / 16;           // 16-channel steps (S^T contraction)
+    constexpr int DT = D / 32;           // 32-channel tiles (O^T rows)
+    constexpr float kTau = 8.0f;         // lazy-rescale threshold (log2 units)
+    __shared__ u32x4_t sK[2][SK * KCH];
+    __shared__ u32x4_t sV[2][D * VCH];
 
     const DevPlan& p = a.p;
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -89,12 +113,12 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
-    const int qrow = wave * 32 + j;    // query row within the block
+    const int qrow = wave * 32 + j;      // query row within the block
 
     // Q^T operand: lane (j, hf) holds channels 16s + 8hf .. +8 of row qrow
     bf16x8_t qop[DS];
     {
-        const uint4* qp = a.q + ((bh * p.Np) + (int64_t)qb * BLK + qrow) * KCH;
+        const u32x4_t* qp = a.q + ((bh * p.Np) + (int64_t)qb * BLK + qrow) * KCH;
 #pragma unroll
         for (int s = 0; s < DS; ++s) qop[s] = as_bf16x8(qp[2 * s + hf]);
     }
@@ -113,112 +137,134 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnArgs a) {
     const int32_t* cl = dense ? nullptr : a.col + bh * p.nnz_per_head + r0;
     const int last_video = p.nB_video - 1;
     const int last_valid = p.blk_valid[last_video];
+    const u32x4_t* kbase = a.k + bh * p.Np * KCH;
+    const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (D * BLK / 8);
+    const int nstage = len * SPB;
 
-    for (int it = 0; it < len; ++it) {
-        const int kb = dense ? it : cl[it];
-        if (kb < 0 || kb >= p.nB) continue;           // ignore out-of-range entries
-        __syncthreads();                              // LDS free from the last block
-        {
-            const uint4* gk = a.k + (bh * p.Np + (int64_t)kb * BLK) * KCH;
-#pragma unroll
-            for (int i = 0; i < BLK * KCH / NT; ++i) {
-                const int cidx = tid + i * NT;
-                const int r = cidx / KCH, ch = cidx % KCH;
-                sK[r * KCH + (ch ^ (r & (KCH - 1) & 15))] = gk[cidx];
-            }
-            const uint4* gv = a.vt + (bh * p.nB + kb) * (int64_t)(D * BLK / 8);
-#pragma unroll
-            for (int i = 0; i < D * BLK / 8 / NT; ++i) {
-                const int cidx = tid + i * NT;
-                const int r = cidx / (BLK / 8), ch = cidx % (BLK / 8);
-                const uint4 v = gv[cidx];
-                const int x = r & (VU - 1);
-                sV[r * VU + ((2 * ch) ^ x)] = make_uint2(v.x, v.y);
-                sV[r * VU + ((2 * ch + 1) ^ x)] = make_uint2(v.z, v.w);
-            }
-        }
-        __syncthreads();
+    u32x4_t pk[KPT], pv[VPT];
+#define SVA_STAGE_KB(st) \
+    ([&] { const int kb_ = dense ? (st) / SPB : cl[(st) / SPB]; \
+           return (kb_ >= 0 && kb_ < p.nB) ? kb_ : -1; }())
+#define SVA_LOAD_STAGE(st)                                                            \
+    do {                                                                              \
+        const int kb_ = SVA_STAGE_KB(st);                                             \
+        const int kbc_ = kb_ < 0 ? 0 : kb_;                                           \
+        const int half_ = (st) % SPB;                                                 \
+        const u32x4_t* gk_ = kbase + ((int64_t)kbc_ * BLK + half_ * SK) * KCH;          \
+        const u32x4_t* gv_ = vbase + (int64_t)kbc_ * (D * BLK / 8) + half_ * VCH;       \
+        _Pragma("unroll") for (int i = 0; i < KPT; ++i) pk[i] = gk_[tid + i * NT];    \
+        _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                             \
+            const int q_ = tid + i * NT;                                              \
+            pv[i] = gv_[(q_ / VCH) * (BLK / 8) + (q_ % VCH)];                         \
+        }                                                                             \
+    } while (0)
+#define SVA_STORE_STAGE(buf)                                                          \
+    do {                                                                              \
+        _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                             \
+            const int q_ = tid + i * NT;                                              \
+            const int r_ = q_ / KCH, ch_ = q_ % KCH;                                  \
+            sK[buf][r_ * KCH + swz<KRB>(ch_, r_)] = pk[i];                            \
+        }                                                                             \
+        _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                             \
+            const int q_ = tid + i * NT;                                              \
+            const int r_ = q_ / VCH, ch_ = q_ % VCH;                                  \
+            sV[buf][r_ * VCH + swz<128>(ch_, r_)] = pv[i];                            \
+        }                                                                             \
+    } while (0)
 
-        // S^T = K Q^T: tile kt covers keys kt*32..+32; lane (j, hf) gets
-        // keys kt*32 + 8*(v/4) + 4*hf + v%4 of query column qrow.
-        f32x16_t st[KT];
+    if (nstage > 0) {
+        SVA_LOAD_STAGE(0);
+        SVA_STORE_STAGE(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < nstage; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nstage) SVA_LOAD_STAGE(st + 1);
+        const int kb = SVA_STAGE_KB(st);
+        if (kb >= 0) {
+            const int half = st % SPB;
+            // S^T = K Q^T: tile kt covers stage keys kt*32..+32; lane (j, hf)
+            // gets keys kt*32 + 8*(v/4) + 4*hf + v%4 of query column qrow.
+            f32x16_t sc[2];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) st[kt][v] = 0.f;
-            const int r = kt * 32 + j;
+                for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
+                const int r = kt * 32 + j;
 #pragma unroll
-            for (int s = 0; s < DS; ++s) {
-                const uint4 kv = sK[r * KCH + ((2 * s + hf) ^ (r & (KCH - 1) & 15))];
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[s], st[kt],
-                                                                 0, 0, 0);
+                for (int s = 0; s < DS; ++s) {
+                    const u32x4_t kv = sK[buf][r * KCH + swz<KRB>(2 * s + hf, r)];
+                    sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[s],
+                                                                     sc[kt], 0, 0, 0);
+                }
             }
-        }
-        if (kb == last_video && last_valid < BLK) {   // padding keys of the last video block
+            if (kb == last_video && last_valid < BLK) {   // padding keys
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = half * SK + kt * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
+                        if (key >= last_valid) sc[kt][v] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
+            mx = lane_swap_max(mx) * c;
+            if (__any(mx > m + kTau)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
+            }
+            bf16x8_t pb[2][2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int key = kt * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
-                    if (key >= last_valid) st[kt][v] = -INFINITY;
+                    const float e = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], c, -m));
+                    sc[kt][v] = e;
+                    l += e;
                 }
-        }
-        // online softmax (log2 domain)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[kt][v]);
-        mx = lane_swap_max(mx) * c;
-        const float m_new = fmaxf(m, mx);
-        const float alpha = exp2f(m - m_new);
-        m = m_new;
-        float rs = 0.f;
-        bf16x8_t pb[KT][2];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float e = exp2f(fmaf(st[kt][v], c, -m_new));
-                st[kt][v] = e;
-                rs += e;
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint4 u;
-                u.x = pack_bf16x2(st[kt][8 * s2 + 0], st[kt][8 * s2 + 1]);
-                u.y = pack_bf16x2(st[kt][8 * s2 + 2], st[kt][8 * s2 + 3]);
-                u.z = pack_bf16x2(st[kt][8 * s2 + 4], st[kt][8 * s2 + 5]);
-                u.w = pack_bf16x2(st[kt][8 * s2 + 6], st[kt][8 * s2 + 7]);
-                pb[kt][s2] = as_bf16x8(u);
-            }
-        }
-        l = l * alpha + rs;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-
-        // O^T += V^T P^T.  Step (kt, s2) contracts keys
-        // kt*32 + 16*s2 + {4hf..4hf+3, 8+4hf..8+4hf+3} for lane half hf,
-        // which are 8-byte units u0 = kt*8 + 4*s2 + hf and u0 + 2 of a V^T row.
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const int r = t * 32 + j;
-            const int x = r & (VU - 1);
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const int u0 = kt * 8 + 4 * s2 + hf;
-                    const uint2 lo = sV[r * VU + (u0 ^ x)];
-                    const uint2 hi = sV[r * VU + ((u0 + 2) ^ x)];
-                    const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb[kt][s2],
-                                                                   o[t], 0, 0, 0);
+                    u32x4_t u;
+                    u.x = pack_bf16x2(sc[kt][8 * s2 + 0], sc[kt][8 * s2 + 1]);
+                    u.y = pack_bf16x2(sc[kt][8 * s2 + 2], sc[kt][8 * s2 + 3]);
+                    u.z = pack_bf16x2(sc[kt][8 * s2 + 4], sc[kt][8 * s2 + 5]);
+                    u.w = pack_bf16x2(sc[kt][8 * s2 + 6], sc[kt][8 * s2 + 7]);
+                    pb[kt][s2] = as_bf16x8(u);
                 }
+            }
+            // O^T += V^T P^T.  Step (kt, s2) contracts the 16 stage keys
+            // kt*32 + 16*s2 + ..; lane half hf's 8 of them are V^T storage
+            // chunk 2*(2kt + s2) + hf of the row.
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const int r = t * 32 + j;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const u32x4_t vv = sV[buf][r * VCH + swz<128>(2 * (2 * kt + s2) + hf, r)];
+                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb[kt][s2],
+                                                                       o[t], 0, 0, 0);
+                    }
+            }
         }
+        if (st + 1 < nstage) SVA_STORE_STAGE(buf ^ 1);
+        __syncthreads();
     }
+#undef SVA_STAGE_KB
+#undef SVA_LOAD_STAGE
+#undef SVA_STORE_STAGE
 
     // epilogue: O = O^T / l, padding query rows zero
     const float lt = lane_swap_sum(l);
@@ -243,9 +289,9 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
                             const uint16_t* vt, const int32_t* col, uint16_t* o, hipStream_t s) {
     AttnArgs a;
     a.p = p;
-    a.q = reinterpret_cast<const uint4*>(qr);
-    a.k = reinterpret_cast<const uint4*>(kr);
-    a.vt = reinterpret_cast<const uint4*>(vt);
+    a.q = reinterpret_cast<const u32x4_t*>(qr);
+    a.k = reinterpret_cast<const u32x4_t*>(kr);
+    a.vt = reinterpret_cast<const u32x4_t*>(vt);
     a.col = col;
     a.o = reinterpret_cast<uint2*>(o);
     dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));

@@ -34,18 +34,18 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     constexpr int RPB = kThreads / LPR;        // rows per block per step
     const int tensor = blockIdx.y;
     const DevPlan& p = a.p;
-    const uint4* in = reinterpret_cast<const uint4*>(a.in[tensor]);
-    uint4* out = reinterpret_cast<uint4*>(a.out[tensor]);
+    const u32x4* in = reinterpret_cast<const u32x4*>(a.in[tensor]);
+    u32x4* out = reinterpret_cast<u32x4*>(a.out[tensor]);
     const float* __restrict__ w = a.w[tensor];
     const int sub = threadIdx.x % LPR;
     const int64_t rows = (int64_t)p.B * p.N * p.H;
     const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
 
-    uint4 x[kRows];
+    u32x4 x[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
         const int64_t row = row0 + (int64_t)r * RPB;
-        x[r] = row < rows ? in[row * LPR + sub] : make_uint4(0, 0, 0, 0);
+        x[r] = row < rows ? in[row * LPR + sub] : u32x4{0u, 0u, 0u, 0u};
     }
     const int hw = p.Hh * p.W;
     const float inv_d = 1.0f / D;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
             }
             ob[e] = pack_bf16x2(y0 * c - y1 * s, y0 * s + y1 * c);
         }
-        out[row * LPR + sub] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        out[row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
     }
 }
 

@@ -8,8 +8,9 @@
 //   forward     raster [B,N,H,d] -> tile order [B,H,Np,d], padding zeroed
 //   inverse     tile order -> raster, padding dropped
 //   forward_vt  raster -> V tiles [B,H,nB,d,block]: each block of V stored
-//               transposed, the layout the attention kernel reads V in
-//               (channel-major rows of `block` keys).
+//               transposed (channel-major rows of `block` keys, keys
+//               interleaved inside groups of 16), the layout the attention
+//               kernel reads V in.
 // All three move every byte once and are bound by HBM bandwidth.  Rows are
 // d·2 = 128 or 256 contiguous bytes, so gathers stay at full-line width.
 #include "kernels.h"
@@ -23,20 +24,20 @@ constexpr int kRows = 4;
 
 // Forward: one output row (b, h, p) per d/8 lanes.
 template <int D>
-__global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const uint4* in,
-                                                               uint4* out) {
+__global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const u32x4* in,
+                                                               u32x4* out) {
     constexpr int LPR = D / 8;
     constexpr int RPB = kThreads / LPR;
     const int sub = threadIdx.x % LPR;
     const int64_t rows = (int64_t)p.B * p.H * p.Np;
     const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
-    uint4 v[kRows];
+    u32x4 v[kRows];
     int64_t dst[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
         const int64_t row = row0 + (int64_t)r * RPB;
         dst[r] = row;
-        v[r] = make_uint4(0, 0, 0, 0);
+        v[r] = u32x4{0u, 0u, 0u, 0u};
         if (row < rows) {
             const int64_t pos = row % p.Np;
             const int64_t bh = row / p.Np;
@@ -54,14 +55,14 @@ __global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const 
 // Inverse: one output raster row (b, n, h) per d/8 lanes; writes are
 // contiguous, reads gather whole rows.
 template <int D>
-__global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const uint4* in,
-                                                               uint4* out) {
+__global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const u32x4* in,
+                                                               u32x4* out) {
     constexpr int LPR = D / 8;
     constexpr int RPB = kThreads / LPR;
     const int sub = threadIdx.x % LPR;
     const int64_t rows = (int64_t)p.B * p.N * p.H;
     const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
-    uint4 v[kRows];
+    u32x4 v[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
         const int64_t row = row0 + (int64_t)r * RPB;
@@ -82,13 +83,16 @@ __global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const 
 }
 
 // Forward into V tiles.  One workgroup per (b, h, block): thread (kg, dc)
-// loads keys kg*8..kg*8+7 of channel chunk dc (8 rows of 16 bytes), turns
-// the 8×8 bf16 square around in registers and writes channels dc*8..dc*8+7
-// of those 8 keys (8 rows of 16 bytes of the transposed tile).
+// gathers the 8 keys of storage chunk kg for channel chunk dc (8 rows of 16
+// bytes), turns the 8×8 bf16 square around in registers and writes
+// channels dc*8..dc*8+7 of that chunk (8 rows of 16 bytes of the tile).
+// Storage order of the keys inside every group of 16 (the order in which
+// the attention kernel's MFMA operand consumes them): chunk 2g holds keys
+// 16g + {0,1,2,3,8,9,10,11}, chunk 2g+1 holds keys 16g + {4,5,6,7,12,13,14,15}.
 template <int D, int BLK>
 __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan p,
-                                                                       const uint4* in,
-                                                                       uint4* out) {
+                                                                       const u32x4* in,
+                                                                       u32x4* out) {
     constexpr int DC = D / 8;      // channel chunks per row
     const int dc = threadIdx.x % DC;
     const int kg = threadIdx.x / DC;
@@ -96,16 +100,18 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
     const int64_t bh = blockIdx.x / p.nB;
     const int h = (int)(bh % p.H);
     const int64_t b = bh / p.H;
+    const int key0 = 16 * (kg >> 1) + 4 * (kg & 1);
     uint32_t m[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int64_t pos = (int64_t)kb * BLK + kg * 8 + j;
+        const int key = key0 + (j & 3) + 8 * (j >> 2);
+        const int64_t pos = (int64_t)kb * BLK + key;
         const int n = p.inv[pos];
-        uint4 v = make_uint4(0, 0, 0, 0);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (n >= 0) v = in[((b * p.N + n) * p.H + h) * DC + dc];
         m[j][0] = v.x; m[j][1] = v.y; m[j][2] = v.z; m[j][3] = v.w;
     }
-    uint4* dst = out + ((bh * p.nB + kb) * D + dc * 8) * (BLK / 8) + kg;
+    u32x4* dst = out + ((bh * p.nB + kb) * D + dc * 8) * (BLK / 8) + kg;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         uint32_t o[4];
@@ -115,7 +121,7 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
             o[w] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
                            : ((lo & 0xffffu) | (hi << 16));
         }
-        dst[e * (BLK / 8)] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[e * (BLK / 8)] = u32x4{o[0], o[1], o[2], o[3]};
     }
 }
 
@@ -123,8 +129,8 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
 
 hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
                           hipStream_t s) {
-    const uint4* i4 = reinterpret_cast<const uint4*>(in);
-    uint4* o4 = reinterpret_cast<uint4*>(out);
+    const u32x4* i4 = reinterpret_cast<const u32x4*>(in);
+    u32x4* o4 = reinterpret_cast<u32x4*>(out);
     const int lpr = p.d / 8;
     const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
     if (direction == 0) {

@@ -29,8 +29,8 @@ namespace {
 constexpr int kPoolThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const uint4* qr,
-                                                            const uint4* kr, double* qmean,
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const u32x4* qr,
+                                                            const u32x4* kr, double* qmean,
                                                             double* kmeanT) {
     constexpr int LPR = D / 8;
     constexpr int RG = kPoolThreads / LPR;   // row groups
@@ -38,13 +38,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const uin
     const int tensor = blockIdx.y;
     const int kb = blockIdx.x % p.nB;
     const int64_t bh = blockIdx.x / p.nB;
-    const uint4* src = (tensor == 0 ? qr : kr) + (bh * p.Np + (int64_t)kb * p.block) * LPR;
+    const u32x4* src = (tensor == 0 ? qr : kr) + (bh * p.Np + (int64_t)kb * p.block) * LPR;
     const int dc = threadIdx.x % LPR;
     const int rg = threadIdx.x / LPR;
     const int valid = p.blk_valid[kb];
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int r = rg; r < valid; r += RG) {
-        const uint4 v = src[(int64_t)r * LPR + dc];
+        const u32x4 v = src[(int64_t)r * LPR + dc];
         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -212,8 +212,8 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     double* kmeanT = ws + BH * p.nB * p.d;
     {
         dim3 grid((unsigned)(BH * p.nB), 2);
-        const uint4* q4 = reinterpret_cast<const uint4*>(qr);
-        const uint4* k4 = reinterpret_cast<const uint4*>(kr);
+        const u32x4* q4 = reinterpret_cast<const u32x4*>(qr);
+        const u32x4* k4 = reinterpret_cast<const u32x4*>(kr);
         if (p.d == 128)
             hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, s, p, q4, k4, qmean, kmeanT);
         else

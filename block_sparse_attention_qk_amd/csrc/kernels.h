@@ -45,6 +45,9 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
 
 // ---- small device helpers shared by the kernels ----
 
+// Native clang vectors (not HIP's uint4 struct): arrays of them stay in
+// registers where arrays of the struct can end up in scratch or LDS.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 

@@ -30,7 +30,12 @@
  *      raster      [B, N, H, d]    token n = (t·Hh + h)·W + w, then extras
  *      tile order  [B, H, Np, d]   Q, K and O after sva_reorder
  *      V tiles     [B, H, nB, d, block]   V after SVA_FORWARD_VT: each key
- *                                  block stored transposed (channel-major)
+ *                                  block stored transposed (channel-major);
+ *                                  inside every group of 16 key slots, slots
+ *                                  0-3 hold keys 0-3, 4-7 keys 8-11, 8-11
+ *                                  keys 4-7 and 12-15 keys 12-15 of the group
+ *                                  (the order the attention kernel's matrix
+ *                                  instructions consume them in)
  *  - Np = n_video rounded up to a multiple of block, plus n_extra; nB =
  *    Np / block.  Padding rows of a tile-ordered tensor are zero.
  *  - Compute calls only enqueue work on `stream` (a hipStream_t; NULL is the

@@ -72,13 +72,17 @@ def small_case(name):
     return _cache[name]
 
 
+# Key order inside every group of 16 key slots of a V tile (the header's
+# V-tile layout): slots 0-3 hold keys 0-3, 4-7 keys 8-11, 8-11 keys 4-7,
+# 12-15 keys 12-15.
+_VT_KEY_ORDER = np.array([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15])
+
+
 def _vt_from_vr(vr_bits, g):
-    """[Np, d] tile-ordered rows -> [nB, d, block] transposed blocks."""
-    return np.ascontiguousarray(vr_bits.reshape(g.nB, g.block, g.d).transpose(0, 2, 1))
-
-
-def _vr_from_vt(vt_bits, g):
-    return np.ascontiguousarray(vt_bits.transpose(0, 2, 1).reshape(g.Np, g.d))
+    """[Np, d] tile-ordered rows -> [nB, d, block] V tiles."""
+    keys = (np.arange(g.block) // 16) * 16 + _VT_KEY_ORDER[np.arange(g.block) % 16]
+    blocks = vr_bits.reshape(g.nB, g.block, g.d)[:, keys, :]
+    return np.ascontiguousarray(blocks.transpose(0, 2, 1))
 
 
 def _col_from_kept(kept_per_bh, g, B, H):
