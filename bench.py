@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan720p_sp75")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "kernel that scales the profiler's byte counters)")
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="heads the CPU oracle runs the whole step on (bounded sample)")
     return ap.parse_args()
@@ -80,14 +83,16 @@ def main():
         S.sva_qk_norm_rope(plan, dq, dk, dwq, dwk, buf.qn, buf.kn)
         rec(1)
         S.sva_reorder(plan, buf.qn, buf.q_r, S.SVA_FORWARD)
-        S.sva_reorder(plan, buf.kn, buf.k_r, S.SVA_FORWARD)
+        S.sva_reorder(plan, buf.kn, buf.k_t, S.SVA_FORWARD_KT)
+        if not info.dense:
+            S.sva_reorder(plan, buf.kn, buf.k_r, S.SVA_FORWARD)
         rec(2)
         S.sva_reorder(plan, dv, buf.v_t, S.SVA_FORWARD_VT)
         rec(3)
         if not info.dense:
             S.sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col)
         rec(4)
-        S.sva_attention(plan, buf.q_r, buf.k_r, buf.v_t, buf.col, buf.o_r)
+        S.sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r)
         rec(5)
         S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
         rec(6)
@@ -95,6 +100,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # timed region: exactly `steps` steps, per-stage HIP events on the stream
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]

@@ -31,6 +31,7 @@ SVA_KEEP_SAME_FRAME = 2
 SVA_FORWARD = 0
 SVA_INVERSE = 1
 SVA_FORWARD_VT = 2
+SVA_FORWARD_KT = 3
 
 EXPORTED = (
     "sva_plan_desc_init", "sva_plan_query", "sva_plan_host_tables",
@@ -212,7 +213,12 @@ class Plan:
     @property
     def vt_shape(self):
         d = self.desc
-        return (d.B, d.H, int(self.info.nB), d.d, d.block)
+        return (d.B, d.H, int(self.info.nB), d.block // 32, 4, d.d, 8)
+
+    @property
+    def kt_shape(self):
+        d = self.desc
+        return (d.B, d.H, int(self.info.nB), d.block // 32, d.d // 16, 64, 8)
 
     def host_tables(self, forced=False):
         return sva_plan_host_tables(self.desc, forced)
@@ -263,6 +269,8 @@ def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
         si, so = plan.tile_shape, plan.raster_shape
     elif direction == SVA_FORWARD_VT:
         si, so = plan.raster_shape, plan.vt_shape
+    elif direction == SVA_FORWARD_KT:
+        si, so = plan.raster_shape, plan.kt_shape
     else:
         raise ValueError("unknown direction")
     _check(lib().sva_reorder(plan.handle, _tensor(inp, si, torch.bfloat16, "in"),
@@ -284,7 +292,7 @@ def sva_select_blocks(plan: Plan, q_r, k_r, workspace, col, stream=None) -> None
                                    _stream(stream)))
 
 
-def sva_attention(plan: Plan, q_r, k_r, v_t, col, o_r, stream=None) -> None:
+def sva_attention(plan: Plan, q_r, k_t, v_t, col, o_r, stream=None) -> None:
     import torch
     ts = plan.tile_shape
     c = None
@@ -293,7 +301,7 @@ def sva_attention(plan: Plan, q_r, k_r, v_t, col, o_r, stream=None) -> None:
     elif not plan.info.dense:
         raise ValueError("col is required for a sparse plan")
     _check(lib().sva_attention(plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r"),
-                               _tensor(k_r, ts, torch.bfloat16, "k_r"),
+                               _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
                                _tensor(v_t, plan.vt_shape, torch.bfloat16, "v_t"), c,
                                _tensor(o_r, ts, torch.bfloat16, "o_r"), _stream(stream)))
 
@@ -320,6 +328,7 @@ class Buffers:
         self.kn = torch.empty(plan.raster_shape, dtype=bf, device=device)
         self.q_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
         self.k_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
+        self.k_t = torch.empty(plan.kt_shape, dtype=bf, device=device)
         self.v_t = torch.empty(plan.vt_shape, dtype=bf, device=device)
         self.o_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
         self.o = torch.empty(plan.raster_shape, dtype=bf, device=device)
@@ -334,10 +343,11 @@ def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
     reorder.  Returns the raster output tensor ``buf.o``."""
     sva_qk_norm_rope(plan, q, k, wq, wk, buf.qn, buf.kn, stream)
     sva_reorder(plan, buf.qn, buf.q_r, SVA_FORWARD, stream)
-    sva_reorder(plan, buf.kn, buf.k_r, SVA_FORWARD, stream)
+    sva_reorder(plan, buf.kn, buf.k_t, SVA_FORWARD_KT, stream)
     sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
     if not plan.info.dense:
+        sva_reorder(plan, buf.kn, buf.k_r, SVA_FORWARD, stream)
         sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col, stream)
-    sva_attention(plan, buf.q_r, buf.k_r, buf.v_t, buf.col, buf.o_r, stream)
+    sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r, stream)
     sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
     return buf.o

@@ -9,35 +9,40 @@
 // attention ("SVA_DENSE", the dense warm-up steps of the same page).
 //
 // Work split: one workgroup per (b, h, qb), one wave per 32 query rows
-// (BLK/32 waves), two workgroups per CU (64 KB of LDS and <= 256 registers
-// per wave each), so every SIMD holds two waves whose MFMA and softmax
-// phases interleave.  A row's key blocks are consumed in stages of 64
-// keys; the workgroup keeps two LDS stage buffers and issues the global
-// loads of stage s+1 into registers before computing stage s, writing them
-// to the other buffer afterwards (one barrier per stage).  Per stage each
-// wave computes
-//   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries
+// (BLK/32 waves), two workgroups per CU.  A row's key blocks are consumed
+// in stages of 32 keys.  Both operand streams come in MFMA-ready tile
+// layouts written by the reorder kernels (K tiles, V tiles), in which one
+// stage of K and one stage of V are each a contiguous span of 32·d bf16.
+// They are copied into LDS as they are, with global_load_lds_dwordx4 (each
+// wave-level load moves 1 KB, lane l to byte 16 l), into three rotating
+// buffer pairs: the loads for stage st + 2 are issued before stage st is
+// computed, and an iteration ends by waiting for stage st + 1 only (vmcnt;
+// the loads of st + 2 stay in flight) and one barrier.  Per stage each wave
+// computes
+//   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries; the
+//                    operand of lane l for channel step s is the 16 bytes at
+//                    (s·64 + l)·16 of the K stage
 //   softmax on S^T   each lane owns one query column: row max and sums are
-//                    lane-local plus one exchange between the two lane halves
+//                    lane-local plus one exchange between the two lane
+//                    halves (v_permlane32_swap)
 //   O^T += V^T · P^T v_mfma_f32_32x32x16_bf16, M = channels, N = queries;
 //                    P^T comes straight from the S^T accumulators; the V
-//                    tiles store keys in the order that accumulator layout
-//                    hands them over (see the V-tile reorder), so each V
-//                    operand is one 16-byte LDS read.
+//                    stage holds four chunks of 8 keys, each chunk as d rows
+//                    of 16 bytes, with the keys in the order that accumulator
+//                    layout hands them over (see the V-tile reorder).
+// Lanes 0-31 and 32-63 of every LDS read touch 32 consecutive 16-byte slots
+// each, which the LDS serves without bank conflicts; every read address is
+// one per-lane base plus an immediate offset, and the copies need no
+// per-lane address arithmetic beyond base + 16 l.
 // Logits are scaled by log2(e)/sqrt(d) and exponentiated with v_exp_f32.
 // The running max is raised only when a row's new max exceeds it by more
 // than 8 (log2 units); in between, probabilities are taken against the
 // stale max (at most 2^8, exact in the final division), which skips most
 // rescales of the accumulator.
 //
-// LDS layouts avoid bank conflicts with XOR swizzles of 16-byte chunks: a
-// row of 256 bytes puts chunk c at c ^ (r mod 16), a row of 128 bytes at
-// c ^ ((r/2) mod 8), so the 16 lanes served together read 16 different bank
-// groups.
-//
 // Roofline: 4·BLK²·d flops per (query block, key block) pair on the MFMA
 // pipe (8.4 MFLOP at BLK = d = 128) against 2·BLK·d·2 bytes of K and V
-// staged (64 KB): 128 flop/byte, which L2 / Infinity Cache reuse across
+// (64 KB): 128 flop/byte, which L2 / Infinity Cache reuse across
 // neighbouring query blocks of a head has to serve.
 #include "kernels.h"
 
@@ -52,8 +57,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 struct AttnArgs {
     DevPlan p;
     const u32x4_t* q;    // [B,H,Np,d]
-    const u32x4_t* k;    // [B,H,Np,d]
-    const u32x4_t* vt;   // [B,H,nB,d,BLK]
+    const u32x4_t* k;    // K tiles [B,H,nB,BLK/32,d/16,64,8]
+    const u32x4_t* vt;   // V tiles [B,H,nB,BLK/32,4,d,8]
     const int32_t* col;  // [B,H,nnz_per_head]
     uint2* o;            // [B,H,Np,d]
 };
@@ -82,29 +87,73 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t n) {
     return x * per + (x < rem ? x : rem) + idx;
 }
 
-// 16-byte chunk slot of chunk c in LDS row r (rows of RB bytes).
-template <int RB>
-__device__ __forceinline__ int swz(int c, int r) {
-    if constexpr (RB == 256) return c ^ (r & 15);
-    else return c ^ ((r >> 1) & 7);
+// One 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4): lane l
+// writes LDS bytes [lds + 16 l, lds + 16 l + 16).  Issued from asm so the
+// compiler's wait-count pass does not track it: that pass cannot tell the
+// rotating stage buffers apart across the unrolled loop and would wait for
+// every stage in flight before each LDS read.  The kernel waits for these
+// loads itself (vmcnt, in issue order).  No register outputs; M0 is set in
+// the same block, with one wait state before the load reads it.  The
+// compiler treats M0 as reserved and does not honour the clobber; nothing
+// else in these kernels uses M0 (gfx950 LDS instructions do not read it),
+// which the compiled code of every instantiation confirms.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_addr)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left unconstrained.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+
+// Stage buffer pairs (K and V, 2·32·d bf16 each): four, so the copies run
+// three stages ahead, while two workgroups of a CU still fit in its LDS.
+// With d = 128 and 64-token blocks a workgroup has only two waves; there
+// three pairs (48 KB) let three workgroups share a CU.
+#ifndef SVA_STAGE_BUFFERS
+#define SVA_STAGE_BUFFERS 4
+#endif
+constexpr int attn_stage_buffers(int d, int blk) {
+    return (d == 128 && blk == 64) ? 3 : SVA_STAGE_BUFFERS;
+}
+// waves per SIMD the register budget is sized for (LDS decides the rest)
+constexpr int attn_min_waves(int d, int blk) { return (d == 128 && blk == 64) ? 1 : 2; }
+
+template <int D, int BLK, bool DENSE>
+__global__ __launch_bounds__(BLK * 2)
+__attribute__((amdgpu_waves_per_eu(attn_min_waves(D, BLK), 2)))
 void attn_kernel(AttnArgs a) {
     constexpr int NT = BLK * 2;          // threads (BLK/32 waves)
-    constexpr int SK = 64;               // keys per stage
+    constexpr int NWV = NT / 64;
+    constexpr int SK = 32;               // keys per stage (one 32-key MFMA tile)
     constexpr int SPB = BLK / SK;        // stages per block
-    constexpr int KCH = D / 8;           // 16-byte chunks per K row
-    constexpr int KRB = D * 2;           // bytes per K row
-    constexpr int VCH = SK / 8;          // 16-byte chunks per V^T stage row
-    constexpr int KPT = SK * KCH / NT;   // K chunks per thread per stage
-    constexpr int VPT = D * VCH / NT;    // V chunks per thread per stage
+    constexpr int KCH = D / 8;           // 16-byte chunks per Q row
+    constexpr int CPS = SK * D / 8;      // 16-byte chunks per stage, of K and of V
+    constexpr int LPW = CPS / (64 * NWV);// wave-level copies per wave and operand
     constexpr int DS = D / 16;           // 16-channel steps (S^T contraction)
     constexpr int DT = D / 32;           // 32-channel tiles (O^T rows)
     constexpr float kTau = 8.0f;         // lazy-rescale threshold (log2 units)
-    __shared__ u32x4_t sK[2][SK * KCH];
-    __shared__ u32x4_t sV[2][D * VCH];
+    static_assert(LPW >= 1 && LPW * 64 * NWV == CPS, "stage copy split");
+    constexpr int NBUF = attn_stage_buffers(D, BLK);   // copies run NBUF-1 stages ahead
+    static_assert(NBUF >= 3, "K of stage st+1 is read in iteration st");
+    // vmcnt((NBUF-3)·2·LPW): all but the copies of the NBUF-3 latest stages have landed
+    constexpr int kInFlight = (NBUF - 3) * 2 * LPW;
+    static_assert(kInFlight < 64, "vmcnt range");
+    constexpr int kWaitNext = (kInFlight & 15) | ((kInFlight >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+    __shared__ u32x4_t sK[NBUF][CPS];
+    __shared__ u32x4_t sV[NBUF][CPS];
+    extern __shared__ int32_t s_col[];   // this row's block list (sparse plans)
 
     const DevPlan& p = a.p;
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -114,6 +163,7 @@ void attn_kernel(AttnArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
     const int qrow = wave * 32 + j;      // query row within the block
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
 
     // Q^T operand: lane (j, hf) holds channels 16s + 8hf .. +8 of row qrow
     bf16x8_t qop[DS];
@@ -122,149 +172,194 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < DS; ++s) qop[s] = as_bf16x8(qp[2 * s + hf]);
     }
+    // Drain the Q loads here: vmcnt retires in order, so a wait for Q placed
+    // inside the loop would also wait for the stage copies issued before it.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     f32x16_t o[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[t][v] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    // -1e30 instead of -inf keeps exp2(m_old - m_new) and fully masked
+    // stages free of inf - inf.
+    float m = -1e30f, l = 0.f;
     const float c = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
 
-    const bool dense = p.dense != 0;
     const int64_t r0 = p.row_ptr[qb];
-    const int len = dense ? p.nB : (int)(p.row_ptr[qb + 1] - r0);
-    const int32_t* cl = dense ? nullptr : a.col + bh * p.nnz_per_head + r0;
+    const int len = DENSE ? p.nB : (int)(p.row_ptr[qb + 1] - r0);
+    const int32_t* cl = DENSE ? nullptr : a.col + bh * p.nnz_per_head + r0;
     const int last_video = p.nB_video - 1;
     const int last_valid = p.blk_valid[last_video];
-    const u32x4_t* kbase = a.k + bh * p.Np * KCH;
-    const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (D * BLK / 8);
+    // this lane's 16 bytes of every wave-level copy
+    const u32x4_t* kbase = a.k + bh * (int64_t)p.nB * (SPB * CPS) + lane;
+    const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (SPB * CPS) + lane;
     const int nstage = len * SPB;
-
-    u32x4_t pk[KPT], pv[VPT];
-#define SVA_STAGE_KB(st) \
-    ([&] { const int kb_ = dense ? (st) / SPB : cl[(st) / SPB]; \
-           return (kb_ >= 0 && kb_ < p.nB) ? kb_ : -1; }())
-#define SVA_LOAD_STAGE(st)                                                            \
-    do {                                                                              \
-        const int kb_ = SVA_STAGE_KB(st);                                             \
-        const int kbc_ = kb_ < 0 ? 0 : kb_;                                           \
-        const int half_ = (st) % SPB;                                                 \
-        const u32x4_t* gk_ = kbase + ((int64_t)kbc_ * BLK + half_ * SK) * KCH;          \
-        const u32x4_t* gv_ = vbase + (int64_t)kbc_ * (D * BLK / 8) + half_ * VCH;       \
-        _Pragma("unroll") for (int i = 0; i < KPT; ++i) pk[i] = gk_[tid + i * NT];    \
-        _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                             \
-            const int q_ = tid + i * NT;                                              \
-            pv[i] = gv_[(q_ / VCH) * (BLK / 8) + (q_ % VCH)];                         \
-        }                                                                             \
-    } while (0)
-#define SVA_STORE_STAGE(buf)                                                          \
-    do {                                                                              \
-        _Pragma("unroll") for (int i = 0; i < KPT; ++i) {                             \
-            const int q_ = tid + i * NT;                                              \
-            const int r_ = q_ / KCH, ch_ = q_ % KCH;                                  \
-            sK[buf][r_ * KCH + swz<KRB>(ch_, r_)] = pk[i];                            \
-        }                                                                             \
-        _Pragma("unroll") for (int i = 0; i < VPT; ++i) {                             \
-            const int q_ = tid + i * NT;                                              \
-            const int r_ = q_ / VCH, ch_ = q_ % VCH;                                  \
-            sV[buf][r_ * VCH + swz<128>(ch_, r_)] = pv[i];                            \
-        }                                                                             \
-    } while (0)
-
-    if (nstage > 0) {
-        SVA_LOAD_STAGE(0);
-        SVA_STORE_STAGE(0);
-    }
-    __syncthreads();
-
-    for (int st = 0; st < nstage; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstage) SVA_LOAD_STAGE(st + 1);
-        const int kb = SVA_STAGE_KB(st);
-        if (kb >= 0) {
-            const int half = st % SPB;
-            // S^T = K Q^T: tile kt covers stage keys kt*32..+32; lane (j, hf)
-            // gets keys kt*32 + 8*(v/4) + 4*hf + v%4 of query column qrow.
-            f32x16_t sc[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sc[kt][v] = 0.f;
-                const int r = kt * 32 + j;
-#pragma unroll
-                for (int s = 0; s < DS; ++s) {
-                    const u32x4_t kv = sK[buf][r * KCH + swz<KRB>(2 * s + hf, r)];
-                    sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qop[s],
-                                                                     sc[kt], 0, 0, 0);
-                }
-            }
-            if (kb == last_video && last_valid < BLK) {   // padding keys
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = half * SK + kt * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
-                        if (key >= last_valid) sc[kt][v] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
-            mx = lane_swap_max(mx) * c;
-            if (__any(mx > m + kTau)) {
-                const float m_new = fmaxf(m, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-                m = m_new;
-                l *= alpha;
-#pragma unroll
-                for (int t = 0; t < DT; ++t)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o[t][v] *= alpha;
-            }
-            bf16x8_t pb[2][2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(sc[kt][v], c, -m));
-                    sc[kt][v] = e;
-                    l += e;
-                }
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    u32x4_t u;
-                    u.x = pack_bf16x2(sc[kt][8 * s2 + 0], sc[kt][8 * s2 + 1]);
-                    u.y = pack_bf16x2(sc[kt][8 * s2 + 2], sc[kt][8 * s2 + 3]);
-                    u.z = pack_bf16x2(sc[kt][8 * s2 + 4], sc[kt][8 * s2 + 5]);
-                    u.w = pack_bf16x2(sc[kt][8 * s2 + 6], sc[kt][8 * s2 + 7]);
-                    pb[kt][s2] = as_bf16x8(u);
-                }
-            }
-            // O^T += V^T P^T.  Step (kt, s2) contracts the 16 stage keys
-            // kt*32 + 16*s2 + ..; lane half hf's 8 of them are V^T storage
-            // chunk 2*(2kt + s2) + hf of the row.
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const int r = t * 32 + j;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const u32x4_t vv = sV[buf][r * VCH + swz<128>(2 * (2 * kt + s2) + hf, r)];
-                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb[kt][s2],
-                                                                       o[t], 0, 0, 0);
-                    }
-            }
-        }
-        if (st + 1 < nstage) SVA_STORE_STAGE(buf ^ 1);
+    if (!DENSE) {
+        for (int i = tid; i < len; i += NT) s_col[i] = cl[i];
         __syncthreads();
     }
-#undef SVA_STAGE_KB
-#undef SVA_LOAD_STAGE
-#undef SVA_STORE_STAGE
+
+    // block of stage st (clamped into the row so copies past the end stay in
+    // valid memory); -1 marks an out-of-range list entry
+#define SVA_KB(st)                                                                   \
+    ([&](int sq_) {                                                                  \
+        sq_ = sq_ < nstage ? sq_ : nstage - 1;                                       \
+        const int kq_ = DENSE ? sq_ / SPB : __builtin_amdgcn_readfirstlane(s_col[sq_ / SPB]); \
+        return (kq_ >= 0 && kq_ < p.nB) ? kq_ : -1;                                  \
+    }(st))
+    // copies of stage st into the buffer pair (KB_, VB_)
+#define SVA_DMA(st, KB_, VB_)                                                        \
+    do {                                                                             \
+        const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
+        const int kb_ = SVA_KB(st_);                                                 \
+        const int64_t off_ = ((int64_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * CPS; \
+        _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
+            const int e_ = (i * NWV + wave_u) * 64;                                  \
+            lds_dma16(kbase + off_ + e_, lds_addr(KB_ + e_));                        \
+            lds_dma16(vbase + off_ + e_, lds_addr(VB_ + e_));                        \
+        }                                                                            \
+    } while (0)
+    // S^T of stage st into SC from the K buffer KB_
+#define SVA_SCORE(KB_, SC)                                                           \
+    do {                                                                             \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) SC[v] = 0.f;                  \
+        _Pragma("unroll") for (int s = 0; s < DS; ++s)                               \
+            SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(KB_[s * 64 + lane]), \
+                                                         qop[s], SC, 0, 0, 0);       \
+    } while (0)
+    // number of valid keys of stage st (0 for stages past the end)
+#define SVA_LIM(st)                                                                  \
+    ([&](int sl_) {                                                                  \
+        const int kb_ = SVA_KB(sl_);                                                 \
+        return (sl_ >= nstage || kb_ < 0) ? 0                                        \
+             : (kb_ == last_video ? last_valid - (sl_ % SPB) * SK : SK);             \
+    }(st))
+    // row max of SC over every key
+#define SVA_MAX(SC, MX)                                                              \
+    do {                                                                             \
+        MX = -INFINITY;                                                              \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) MX = fmaxf(MX, SC[v]);        \
+    } while (0)
+    // keys from LIM on to -inf and the row max again (rare: the last video
+    // block, out-of-range list entries, stages past the end).  The masked
+    // max is at most the unmasked one; taking the min keeps the unmasked max
+    // live on both paths, so it stays before the branch, beside the PV
+    // matrix instructions, instead of being merged into one max after it.
+#define SVA_MASK(LIM, SC, MX)                                                        \
+    do {                                                                             \
+        if (LIM < SK) {                                                              \
+            /* lane (j, hf) holds stage keys 8*(v/4) + 4*hf + v%4 of column qrow */  \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) {                         \
+                const int key_ = 8 * (v / 4) + 4 * hf + (v % 4);                     \
+                if (key_ >= LIM) SC[v] = -INFINITY;                                  \
+            }                                                                        \
+            float mm_;                                                               \
+            SVA_MAX(SC, mm_);                                                        \
+            MX = fminf(MX, mm_);                                                     \
+        }                                                                            \
+    } while (0)
+    // raise the running max when MX exceeds it by more than kTau
+#define SVA_RESCALE(MX)                                                              \
+    do {                                                                             \
+        if (__any(MX > m + kTau)) {                                                  \
+            const float mn_ = fmaxf(m, MX);                                          \
+            const float al_ = __builtin_amdgcn_exp2f(m - mn_);                       \
+            m = mn_;                                                                 \
+            l *= al_;                                                                \
+            _Pragma("unroll") for (int t = 0; t < DT; ++t)                           \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) o[t][v] *= al_;           \
+        }                                                                            \
+    } while (0)
+    // probabilities of SC against m, summed into l and packed to bf16 in PB
+#define SVA_EXP(SC, PB)                                                              \
+    do {                                                                             \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                             \
+            const float e_ = __builtin_amdgcn_exp2f(fmaf(SC[v], c, -m));             \
+            SC[v] = e_;                                                              \
+            l += e_;                                                                 \
+        }                                                                            \
+        _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                           \
+            u32x4_t u_;                                                              \
+            u_.x = pack_bf16x2(SC[8 * s2 + 0], SC[8 * s2 + 1]);                      \
+            u_.y = pack_bf16x2(SC[8 * s2 + 2], SC[8 * s2 + 3]);                      \
+            u_.z = pack_bf16x2(SC[8 * s2 + 4], SC[8 * s2 + 5]);                      \
+            u_.w = pack_bf16x2(SC[8 * s2 + 6], SC[8 * s2 + 7]);                      \
+            PB[s2] = as_bf16x8(u_);                                                  \
+        }                                                                            \
+    } while (0)
+    // O^T += V^T P^T from the V buffer VB_.  Step s2 contracts stage keys
+    // 16*s2 + ..; lane half hf's 8 of them are V chunk 2*s2 + hf.
+#define SVA_PV(VB_, PB)                                                              \
+    do {                                                                             \
+        _Pragma("unroll") for (int t = 0; t < DT; ++t)                               \
+        _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                           \
+            const u32x4_t vv_ = VB_[(2 * s2 + hf) * D + t * 32 + j];                 \
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv_), PB[s2],   \
+                                                           o[t], 0, 0, 0);           \
+        }                                                                            \
+    } while (0)
+
+    // Software pipeline, one wave: iteration st computes S^T of stage st+1
+    // while it turns S^T of stage st into probabilities, then O^T += V^T P^T
+    // of stage st while it takes the max of stage st+1.  The matrix
+    // instructions of one half have no dependence on the vector
+    // instructions beside them, so one wave keeps both pipes busy.
+    // Copies run NBUF-1 stages ahead; at the end of iteration st both
+    // buffers of stage st+2 have landed (K of st+2 is read in iteration
+    // st+1).  The loop has no ordinary LDS stores, only copies: after this
+    // wave's wait, a bare s_barrier makes every wave's part visible and
+    // orders every wave's reads of the oldest buffers before the copies
+    // into them.  (__syncthreads() would add a workgroup release fence,
+    // which waits for every outstanding load, the copies still ahead
+    // included.)
+    f32x16_t sc, sn;
+    float mx;
+    bf16x8_t pb[2];
+    if (nstage > 0) {
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u) SVA_DMA(u, sK[u], sV[u]);
+        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        __builtin_amdgcn_s_barrier();
+        const int lim0 = SVA_LIM(0);
+        SVA_SCORE(sK[0], sc);
+        SVA_MAX(sc, mx);
+        SVA_MASK(lim0, sc, mx);
+        mx = lane_swap_max(mx) * c;
+        SVA_RESCALE(mx);
+    }
+    // unrolled by NBUF so every buffer index is a constant
+    for (int st = 0; st < nstage; st += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            if (u == 0 || st + u < nstage) {
+                SVA_DMA(st + u + NBUF - 1, sK[(u + NBUF - 1) % NBUF], sV[(u + NBUF - 1) % NBUF]);
+                const int lim = SVA_LIM(st + u + 1);
+                // one straight-line region: the scheduler interleaves the
+                // matrix and vector halves
+                SVA_SCORE(sK[(u + 1) % NBUF], sn);
+                SVA_EXP(sc, pb);
+                SVA_PV(sV[u], pb);
+                SVA_MAX(sn, mx);
+                SVA_MASK(lim, sn, mx);
+                mx = lane_swap_max(mx) * c;
+                SVA_RESCALE(mx);
+                sc = sn;
+                __builtin_amdgcn_s_waitcnt(kWaitNext);
+                __builtin_amdgcn_s_barrier();
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // no copy left in flight at exit
+#undef SVA_PV
+#undef SVA_EXP
+#undef SVA_RESCALE
+#undef SVA_MASK
+#undef SVA_MAX
+#undef SVA_LIM
+#undef SVA_SCORE
+#undef SVA_DMA
+#undef SVA_KB
 
     // epilogue: O = O^T / l, padding query rows zero
     const float lt = lane_swap_sum(l);
@@ -296,14 +391,19 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
     a.o = reinterpret_cast<uint2*>(o);
     dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
     dim3 block(p.block * 2);
-    if (p.d == 128 && p.block == 128)
-        hipLaunchKernelGGL((attn_kernel<128, 128>), grid, block, 0, s, a);
-    else if (p.d == 128)
-        hipLaunchKernelGGL((attn_kernel<128, 64>), grid, block, 0, s, a);
-    else if (p.block == 128)
-        hipLaunchKernelGGL((attn_kernel<64, 128>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((attn_kernel<64, 64>), grid, block, 0, s, a);
+    const size_t lds = p.dense ? 0 : (size_t)p.max_row_len * sizeof(int32_t);
+    auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a); };
+    if (p.dense) {
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, true>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, true>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, true>);
+        else launch(attn_kernel<64, 64, true>);
+    } else {
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, false>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, false>);
+        else launch(attn_kernel<64, 64, false>);
+    }
     return hipGetLastError();
 }
 

@@ -135,7 +135,7 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.row_ptr = static_cast<const int32_t*>(put(h.row_ptr.data(), h.row_ptr.size() * 4, s_rp));
     d.rope_cs = static_cast<const float2*>(put(h.rope_cs.data(), h.rope_cs.size() * 4, s_rope));
     if (e != hipSuccess) {
-        hipFree(plan->dmem);
+        (void)hipFree(plan->dmem);   // the copy error is the one reported
         delete plan;
         return sva::hip_err(e, "hipMemcpy(plan tables)");
     }
@@ -202,7 +202,8 @@ int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* s
     if (!in || !out) return set_err(SVA_ERR_INVALID_ARG, "in and out must be non-NULL");
     if (!sva::aligned16(in) || !sva::aligned16(out))
         return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-    if (direction != SVA_FORWARD && direction != SVA_INVERSE && direction != SVA_FORWARD_VT)
+    if (direction != SVA_FORWARD && direction != SVA_INVERSE && direction != SVA_FORWARD_VT &&
+        direction != SVA_FORWARD_KT)
         return set_err(SVA_ERR_INVALID_ARG, "unknown reorder direction");
     if (in == out) return set_err(SVA_ERR_INVALID_ARG, "reorder cannot run in place");
     hipError_t e = sva::launch_reorder(plan->dev, static_cast<const uint16_t*>(in),
@@ -231,18 +232,18 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r, void* wor
     return SVA_OK;
 }
 
-int sva_attention(sva_plan plan, const void* q_r, const void* k_r, const void* v_t,
+int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                   const int32_t* col, void* o_r, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
-    if (!q_r || !k_r || !v_t || !o_r)
-        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_r, v_t and o_r must be non-NULL");
+    if (!q_r || !k_t || !v_t || !o_r)
+        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, v_t and o_r must be non-NULL");
     if (!plan->host.info.dense && !col)
         return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
-    if (!sva::aligned16(q_r) || !sva::aligned16(k_r) || !sva::aligned16(v_t) ||
+    if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(v_t) ||
         !sva::aligned16(o_r) || ((uintptr_t)col & 3u))
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
     hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
-                                         static_cast<const uint16_t*>(k_r),
+                                         static_cast<const uint16_t*>(k_t),
                                          static_cast<const uint16_t*>(v_t), col,
                                          static_cast<uint16_t*>(o_r),
                                          static_cast<hipStream_t>(stream));

@@ -29,13 +29,19 @@
  *    device memory owned by the caller:
  *      raster      [B, N, H, d]    token n = (t·Hh + h)·W + w, then extras
  *      tile order  [B, H, Np, d]   Q, K and O after sva_reorder
- *      V tiles     [B, H, nB, d, block]   V after SVA_FORWARD_VT: each key
- *                                  block stored transposed (channel-major);
- *                                  inside every group of 16 key slots, slots
- *                                  0-3 hold keys 0-3, 4-7 keys 8-11, 8-11
- *                                  keys 4-7 and 12-15 keys 12-15 of the group
- *                                  (the order the attention kernel's matrix
- *                                  instructions consume them in)
+ *      V tiles     [B, H, nB, block/32, 4, d, 8]   V after SVA_FORWARD_VT:
+ *                                  each key block as groups of 32 keys, each
+ *                                  group as four chunks of 8 keys, each chunk
+ *                                  channel-major (d rows of 8 keys); chunk
+ *                                  kc holds keys 16(kc/2) + 4(kc%2) +
+ *                                  {0,1,2,3,8,9,10,11} of the group, in that
+ *                                  order (the order the attention kernel's
+ *                                  matrix instructions consume them in)
+ *      K tiles     [B, H, nB, block/32, d/16, 64, 8]   K after SVA_FORWARD_KT:
+ *                                  per 32-key group and 16-channel step s,
+ *                                  64 entries of 8 channels; entry 32·hf + j
+ *                                  holds key j of the group, channels
+ *                                  16s + 8hf .. 16s + 8hf + 7
  *  - Np = n_video rounded up to a multiple of block, plus n_extra; nB =
  *    Np / block.  Padding rows of a tile-ordered tensor are zero.
  *  - Compute calls only enqueue work on `stream` (a hipStream_t; NULL is the
@@ -74,7 +80,8 @@ extern "C" {
 /* ---- sva_reorder directions ---- */
 #define SVA_FORWARD     0  /* raster [B,N,H,d] -> tile order [B,H,Np,d]      */
 #define SVA_INVERSE     1  /* tile order [B,H,Np,d] -> raster [B,N,H,d]      */
-#define SVA_FORWARD_VT  2  /* raster [B,N,H,d] -> V tiles [B,H,nB,d,block]   */
+#define SVA_FORWARD_VT  2  /* raster [B,N,H,d] -> V tiles [B,H,nB,block/32,4,d,8] */
+#define SVA_FORWARD_KT  3  /* raster [B,N,H,d] -> K tiles [B,H,nB,block/32,d/16,64,8] */
 
 typedef struct sva_plan_s* sva_plan;
 
@@ -180,10 +187,11 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r,
 /* Attention over the kept blocks.  For each valid query row p of block qb:
  * o_p = sum_j softmax_j(q_p·k_j / sqrt(d)) v_j over the valid keys j of the
  * blocks in row qb of `col` (any ascending list with the plan's row_ptr is
- * accepted; a dense plan ignores `col`, which may be NULL).  q_r, k_r:
- * [B, H, Np, d]; v_t: V tiles [B, H, nB, d, block]; o_r: [B, H, Np, d],
- * padding rows written as zero. */
-int sva_attention(sva_plan plan, const void* q_r, const void* k_r, const void* v_t,
+ * accepted; entries outside [0, nB) are skipped; a dense plan ignores
+ * `col`, which may be NULL).  q_r: [B, H, Np, d] (SVA_FORWARD of Q');
+ * k_t: K tiles (SVA_FORWARD_KT of K'); v_t: V tiles (SVA_FORWARD_VT of V);
+ * o_r: [B, H, Np, d], padding rows written as zero. */
+int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                   const int32_t* col, void* o_r, void* stream);
 
 /* ---- errors ---- */

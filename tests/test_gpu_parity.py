@@ -72,17 +72,27 @@ def small_case(name):
     return _cache[name]
 
 
-# Key order inside every group of 16 key slots of a V tile (the header's
-# V-tile layout): slots 0-3 hold keys 0-3, 4-7 keys 8-11, 8-11 keys 4-7,
-# 12-15 keys 12-15.
-_VT_KEY_ORDER = np.array([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15])
+# V-tile layout (see the header): each block as groups of 32 keys, each
+# group as four chunks of 8 keys stored channel-major; chunk kc holds keys
+# 16(kc/2) + 4(kc%2) + {0,1,2,3,8,9,10,11}.
+_VT_CHUNK_KEYS = np.array([[16 * (kc // 2) + 4 * (kc % 2) + o for o in (0, 1, 2, 3, 8, 9, 10, 11)]
+                           for kc in range(4)])
 
 
 def _vt_from_vr(vr_bits, g):
-    """[Np, d] tile-ordered rows -> [nB, d, block] V tiles."""
-    keys = (np.arange(g.block) // 16) * 16 + _VT_KEY_ORDER[np.arange(g.block) % 16]
-    blocks = vr_bits.reshape(g.nB, g.block, g.d)[:, keys, :]
-    return np.ascontiguousarray(blocks.transpose(0, 2, 1))
+    """[Np, d] tile-ordered rows -> [nB, block/32, 4, d, 8] V tiles."""
+    groups = vr_bits.reshape(g.nB, g.block // 32, 32, g.d)          # kb, grp, key, ch
+    x = groups[:, :, _VT_CHUNK_KEYS, :]                             # kb, grp, kc, i, ch
+    return np.ascontiguousarray(x.transpose(0, 1, 2, 4, 3))
+
+
+def _kt_from_kr(kr_bits, g):
+    """[Np, d] tile-ordered rows -> [nB, block/32, d/16, 64, 8] K tiles:
+    per 32-key group and 16-channel step s, entry 32*hf + j holds key j,
+    channels 16s + 8hf .. +7."""
+    x = kr_bits.reshape(g.nB, g.block // 32, 32, g.d // 16, 2, 8)   # kb, grp, j, s, hf, c
+    return np.ascontiguousarray(x.transpose(0, 1, 3, 4, 2, 5).reshape(
+        g.nB, g.block // 32, g.d // 16, 64, 8))
 
 
 def _col_from_kept(kept_per_bh, g, B, H):
@@ -124,9 +134,15 @@ def test_reorder_parity(name):
     run = GpuRun(wl, q, k, v, wq, wk)
     S.sva_reorder(run.plan, run.q, run.buf.q_r, S.SVA_FORWARD)
     S.sva_reorder(run.plan, run.v, run.buf.v_t, S.SVA_FORWARD_VT)
+    S.sva_reorder(run.plan, run.k, run.buf.k_t, S.SVA_FORWARD_KT)
     torch.cuda.synchronize()
     want = O.reorder_forward(q, g, perm)                      # uint16 bits move as-is
     assert np.array_equal(host(run.buf.q_r), want)
+    wk_ = O.reorder_forward(k, g, perm)
+    kt = host(run.buf.k_t)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            assert np.array_equal(kt[b, h], _kt_from_kr(wk_[b, h], g))
     wv = O.reorder_forward(v, g, perm)
     vt = host(run.buf.v_t)
     for b in range(wl.B):
@@ -171,16 +187,16 @@ def test_attention_parity(name):
     run = GpuRun(wl, q, k, v, wq, wk)
     B, H = wl.B, wl.H
     qr = np.zeros((B, H, g.Np, g.d), np.uint16)
-    kr = np.zeros_like(qr)
-    vt = np.zeros((B, H, g.nB, g.d, g.block), np.uint16)
+    kt = np.zeros((B, H, g.nB, g.block // 32, g.d // 16, 64, 8), np.uint16)
+    vt = np.zeros((B, H, g.nB, g.block // 32, 4, g.d, 8), np.uint16)
     kept = np.zeros((B, H, g.nB, g.nB), bool)
     for (b, h), r in ref.items():
         qr[b, h] = O.f64_to_bf16_bits(r["qr"])
-        kr[b, h] = O.f64_to_bf16_bits(r["kr"])
+        kt[b, h] = _kt_from_kr(O.f64_to_bf16_bits(r["kr"]), g)
         vt[b, h] = _vt_from_vr(O.f64_to_bf16_bits(r["vr"]), g)
         kept[b, h] = r["kept"]
     col = None if run.plan.info.dense else dev_col(_col_from_kept(kept, g, B, H))
-    S.sva_attention(run.plan, dev(qr), dev(kr), dev(vt), col, run.buf.o_r)
+    S.sva_attention(run.plan, dev(qr), dev(kt), dev(vt), col, run.buf.o_r)
     torch.cuda.synchronize()
     out = host_f64(run.buf.o_r)
     worst_rel, worst_abs = 0.0, 0.0
@@ -303,14 +319,17 @@ def test_full_workload_sampled(name):
             stats["elems"] += t
         # reorder (bit-exact, from the GPU's own prologue output)
         qr_g = host(run.buf.q_r[0, h])
-        kr_g = host(run.buf.k_r[0, h])
+        kt_g = host(run.buf.k_t[0, h])
         vt_g = host(run.buf.v_t[0, h])
         want = np.zeros((g.Np, g.d), np.uint16)
         want[perm] = qn_g
         if not np.array_equal(qr_g, want):
             fails.append(("reorder q", h))
         want[perm] = kn_g
-        if not np.array_equal(kr_g, want):
+        kr_g = want.copy()
+        if not np.array_equal(kt_g, _kt_from_kr(want, g)):
+            fails.append(("reorder k tiles", h))
+        if col is not None and not np.array_equal(host(run.buf.k_r[0, h]), want):
             fails.append(("reorder k", h))
         want[perm] = v[0, :, h]
         if not np.array_equal(vt_g, _vt_from_vr(want, g)):
