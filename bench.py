@@ -84,13 +84,11 @@ def main():
         rec(1)
         S.sva_reorder(plan, buf.qn, buf.q_r, S.SVA_FORWARD)
         S.sva_reorder(plan, buf.kn, buf.k_t, S.SVA_FORWARD_KT)
-        if not info.dense:
-            S.sva_reorder(plan, buf.kn, buf.k_r, S.SVA_FORWARD)
         rec(2)
         S.sva_reorder(plan, dv, buf.v_t, S.SVA_FORWARD_VT)
         rec(3)
         if not info.dense:
-            S.sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col)
+            S.sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col)
         rec(4)
         S.sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r)
         rec(5)

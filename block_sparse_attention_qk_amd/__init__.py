@@ -277,7 +277,7 @@ def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
                              _tensor(out, so, torch.bfloat16, "out"), direction, _stream(stream)))
 
 
-def sva_select_blocks(plan: Plan, q_r, k_r, workspace, col, stream=None) -> None:
+def sva_select_blocks(plan: Plan, q_r, k_t, workspace, col, stream=None) -> None:
     import torch
     if plan.info.dense:
         return
@@ -286,7 +286,7 @@ def sva_select_blocks(plan: Plan, q_r, k_r, workspace, col, stream=None) -> None
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().sva_select_blocks(plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r"),
-                                   _tensor(k_r, ts, torch.bfloat16, "k_r"),
+                                   _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
                                    ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
                                    _tensor(col, (int(plan.info.nnz),), torch.int32, "col"),
                                    _stream(stream)))
@@ -327,7 +327,6 @@ class Buffers:
         self.qn = torch.empty(plan.raster_shape, dtype=bf, device=device)
         self.kn = torch.empty(plan.raster_shape, dtype=bf, device=device)
         self.q_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
-        self.k_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
         self.k_t = torch.empty(plan.kt_shape, dtype=bf, device=device)
         self.v_t = torch.empty(plan.vt_shape, dtype=bf, device=device)
         self.o_r = torch.empty(plan.tile_shape, dtype=bf, device=device)
@@ -346,8 +345,7 @@ def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
     sva_reorder(plan, buf.kn, buf.k_t, SVA_FORWARD_KT, stream)
     sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
     if not plan.info.dense:
-        sva_reorder(plan, buf.kn, buf.k_r, SVA_FORWARD, stream)
-        sva_select_blocks(plan, buf.q_r, buf.k_r, buf.ws, buf.col, stream)
+        sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
     sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r, stream)
     sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
     return buf.o

@@ -38,20 +38,39 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     u32x4* out = reinterpret_cast<u32x4*>(a.out[tensor]);
     const float* __restrict__ w = a.w[tensor];
     const int sub = threadIdx.x % LPR;
-    const int64_t rows = (int64_t)p.B * p.N * p.H;
-    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
+    // row = (b·N + n)·H + h; the plan guarantees fewer than 2^31 rows
+    const uint32_t rows = (uint32_t)(p.B * p.N * p.H);
+    const uint32_t row0 = blockIdx.x * (uint32_t)(RPB * kRows) + threadIdx.x / LPR;
 
     u32x4 x[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const int64_t row = row0 + (int64_t)r * RPB;
-        x[r] = row < rows ? in[row * LPR + sub] : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t row = row0 + r * RPB;
+        x[r] = row < rows ? in[(int64_t)row * LPR + sub] : u32x4{0u, 0u, 0u, 0u};
     }
-    const int hw = p.Hh * p.W;
+
+    // this lane's four channel pairs: RoPE section (-1: not rotated) and the
+    // pair's offset in that section's cos/sin table
+    int pax[4], pbase[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int pi = sub * 4 + e;
+        pax[e] = -1;
+        pbase[e] = 0;
+#pragma unroll
+        for (int ax = 0; ax < 3; ++ax) {
+            const int half = p.rope_half[ax];
+            if (pax[e] < 0 && pi < half) {
+                pax[e] = ax;
+                pbase[e] = p.rope_off[ax] + pi;
+            }
+            pi -= half;
+        }
+    }
     const float inv_d = 1.0f / D;
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const int64_t row = row0 + (int64_t)r * RPB;
+        const uint32_t row = row0 + r * RPB;
         const uint32_t u[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
         float v[8];
 #pragma unroll
@@ -65,12 +84,13 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 #pragma unroll
         for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
         if (row >= rows) continue;
-        const int h = (int)(row % p.H);
-        const int64_t n = (row / p.H) % p.N;
+        const uint32_t tok = fast_div(row, p.div_H);
+        const uint32_t h = row - tok * (uint32_t)p.H;
+        const uint32_t n = tok - fast_div(tok, p.div_N) * (uint32_t)p.N;
         const float rs = rsqrtf(ss * inv_d + p.eps);
         float wv[8];
         if (w) {
-            const float4* wp = reinterpret_cast<const float4*>(w + (int64_t)h * D + sub * 8);
+            const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
             const float4 w0 = wp[0], w1 = wp[1];
             wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
             wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
@@ -83,36 +103,26 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             yb[e] = pack_bf16x2(v[2 * e] * rs * wv[2 * e], v[2 * e + 1] * rs * wv[2 * e + 1]);
+        // grid coordinates (t, h, w) of a video token; extra tokens get none
+        const bool video = n < (uint32_t)p.n_video;
+        const uint32_t pt = fast_div(n, p.div_HW);
+        const uint32_t rem = n - pt * (uint32_t)(p.Hh * p.W);
+        const uint32_t ph = fast_div(rem, p.div_W);
+        const uint32_t pw = rem - ph * (uint32_t)p.W;
         uint32_t ob[4];
-        int pos3[3] = {0, 0, 0};
-        const bool video = n < p.n_video;
-        if (video) {
-            const int nn = (int)n;
-            pos3[0] = nn / hw;
-            const int rem = nn - pos3[0] * hw;
-            pos3[1] = rem / p.W;
-            pos3[2] = rem - pos3[1] * p.W;
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float y0 = bf16lo(yb[e]), y1 = bf16hi(yb[e]);
-            int pi = sub * 4 + e;              // pair index within the row
             float c = 1.f, s = 0.f;
-            if (video) {
-#pragma unroll
-                for (int ax = 0; ax < 3; ++ax) {
-                    const int half = p.rope_half[ax];
-                    if (pi >= 0 && pi < half) {
-                        const float2 cs = p.rope_cs[p.rope_off[ax] + pos3[ax] * half + pi];
-                        c = cs.x;
-                        s = cs.y;
-                    }
-                    pi -= half;
-                }
+            if (video && pax[e] >= 0) {
+                const uint32_t pos = pax[e] == 0 ? pt : (pax[e] == 1 ? ph : pw);
+                const float2 cs = p.rope_cs[pbase[e] + pos * p.rope_half[pax[e]]];
+                c = cs.x;
+                s = cs.y;
             }
             ob[e] = pack_bf16x2(y0 * c - y1 * s, y0 * s + y1 * c);
         }
-        out[row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
+        out[(int64_t)row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
     }
 }
 

@@ -8,14 +8,17 @@
 // reading of "mean-pooled Q and K": s(qb, kb) = mean(Q' of qb) · mean(K' of kb).
 //
 // Two kernels:
-//  pool   one workgroup per (tensor, b, h, block): float64 sums of the
+//  pool   one workgroup per (b, h, block) and tensor: float64 sums of the
 //         valid rows, divided by the valid count.  Sums of at most 128 bf16
 //         values are exact in float64 for the data this sees, so the means
-//         do not depend on summation order.  HBM bound (reads Q' and K'
-//         once).  q means are stored [B,H,nB,d], k means transposed
-//         [B,H,d,nB] so the score loop reads them coalesced.
-//  topk   one workgroup per (b, h, R query blocks): float64 scores of the R
-//         rows against every key block into LDS, then one wave per row
+//         do not depend on summation order.  HBM bound (reads Q' in tile
+//         order and K' as the attention kernel's K tiles, once each).  q
+//         means are stored [B,H,nB,d], k means transposed [B,H,d,nB] so the
+//         score loop reads them coalesced.
+//  topk   one workgroup per (b, h, R <= 8 query blocks): float64 scores of
+//         the R rows against every key block into LDS (each thread walks one
+//         key block's transposed mean with 16 loads in flight, the query
+//         means broadcast from LDS), then one wave per row
 //         finds the r-th largest eligible score by a bitwise search on
 //         order-preserving 64-bit keys (ballot + popcount, no sorting),
 //         takes equal scores lowest index first, and writes the kept
@@ -30,15 +33,13 @@ constexpr int kPoolThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const u32x4* qr,
-                                                            const u32x4* kr, double* qmean,
-                                                            double* kmeanT) {
+                                                            double* qmean) {
     constexpr int LPR = D / 8;
     constexpr int RG = kPoolThreads / LPR;   // row groups
     __shared__ double part[RG][D];
-    const int tensor = blockIdx.y;
     const int kb = blockIdx.x % p.nB;
     const int64_t bh = blockIdx.x / p.nB;
-    const u32x4* src = (tensor == 0 ? qr : kr) + (bh * p.Np + (int64_t)kb * p.block) * LPR;
+    const u32x4* src = qr + (bh * p.Np + (int64_t)kb * p.block) * LPR;
     const int dc = threadIdx.x % LPR;
     const int rg = threadIdx.x / LPR;
     const int valid = p.blk_valid[kb];
@@ -59,11 +60,55 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const u32
         double s = 0.0;
 #pragma unroll 4
         for (int g = 0; g < RG; ++g) s += part[g][threadIdx.x];
-        const double mean = s / (double)valid;
-        if (tensor == 0)
-            qmean[(bh * p.nB + kb) * D + threadIdx.x] = mean;
-        else
-            kmeanT[(bh * D + threadIdx.x) * p.nB + kb] = mean;
+        qmean[(bh * p.nB + kb) * D + threadIdx.x] = s / (double)valid;
+    }
+}
+
+// K means from K tiles: token r = 32g + j of a block sits in entry
+// g·4D + c·32 + j of the block's tile for 8-channel chunk c (channels 8c ..
+// 8c+7).  Thread (j, q) sums chunks q, q + 8, ... over the groups; the 32
+// partial sums of a chunk are added through LDS.
+template <int D, int BLK>
+__global__ __launch_bounds__(kPoolThreads) void pool_kt_kernel(DevPlan p, const u32x4* kt,
+                                                               double* kmeanT) {
+    constexpr int NCH = D / 8;                 // 8-channel chunks
+    constexpr int CPT = NCH / 8;               // chunks per thread
+    constexpr int NG = BLK / 32;               // 32-token groups
+    __shared__ double part[32][D + 1];
+    const int kb = blockIdx.x % p.nB;
+    const int64_t bh = blockIdx.x / p.nB;
+    const u32x4* src = kt + (bh * p.nB + kb) * (int64_t)(BLK * NCH);
+    const int j = threadIdx.x % 32, q = threadIdx.x / 32;
+    const int valid = p.blk_valid[kb];
+    double acc[CPT][8];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        if (g * 32 + j >= valid) break;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const u32x4 v = src[g * 4 * D + (q + 8 * i) * 32 + j];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[i][2 * e] += (double)bf16lo(u[e]);
+                acc[i][2 * e + 1] += (double)bf16hi(u[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[j][(q + 8 * i) * 8 + e] = acc[i][e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        double s = 0.0;
+#pragma unroll 8
+        for (int jj = 0; jj < 32; ++jj) s += part[jj][threadIdx.x];
+        kmeanT[(bh * D + threadIdx.x) * p.nB + kb] = s / (double)valid;
     }
 }
 
@@ -98,9 +143,11 @@ template <int D, int NSLOT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const double* qmean,
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
+    constexpr int RT = 8;              // rows computed per pass over the key means
+    constexpr int DB = 16;             // key-mean loads in flight per thread
     extern __shared__ double smem[];
-    double* qs = smem;                 // [R][D]
-    double* sc = smem + R * D;         // [R][nB]
+    double* qs = smem;                 // [D][RT], rows past nrows zero
+    double* sc = smem + RT * D;        // [R][nB]
     const int nB = p.nB;
     const int groups = (nB + R - 1) / R;
     const int g = blockIdx.x % groups;
@@ -108,22 +155,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     const int qb0 = g * R;
     const int nrows = min(R, nB - qb0);
 
-    for (int i = threadIdx.x; i < nrows * D; i += kTopkThreads)
-        qs[i] = qmean[(bh * nB + qb0) * D + i];
+    for (int i = threadIdx.x; i < RT * D; i += kTopkThreads) {
+        const int dd = i / RT, r = i % RT;
+        qs[i] = r < nrows ? qmean[(bh * nB + qb0 + r) * D + dd] : 0.0;
+    }
     __syncthreads();
 
-    // scores: thread per key block, R rows at once (R <= 8)
+    // scores: thread per key block, all RT rows at once; each score is the
+    // sequential fma chain over the channels
     const double* kt = kmeanT + bh * D * (int64_t)nB;
     for (int kb = threadIdx.x; kb < nB; kb += kTopkThreads) {
-        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int dd = 0; dd < D; ++dd) {
-            const double kv = kt[(int64_t)dd * nB + kb];
+        double acc[RT];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r < nrows) acc[r] = fma(qs[r * D + dd], kv, acc[r]);
+        for (int r = 0; r < RT; ++r) acc[r] = 0.0;
+        for (int d0 = 0; d0 < D; d0 += DB) {
+            double kv[DB];
+#pragma unroll
+            for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nB + kb];
+#pragma unroll
+            for (int i = 0; i < DB; ++i) {
+                const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * RT);
+#pragma unroll
+                for (int r2 = 0; r2 < RT / 2; ++r2) {
+                    const double2 qq = q2[r2];
+                    acc[2 * r2] = fma(qq.x, kv[i], acc[2 * r2]);
+                    acc[2 * r2 + 1] = fma(qq.y, kv[i], acc[2 * r2 + 1]);
+                }
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < RT; ++r)
             if (r < nrows) sc[r * nB + kb] = acc[r];
     }
     __syncthreads();
@@ -205,39 +266,52 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
 
 }  // namespace
 
-hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kr, double* ws,
+hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s) {
     const int64_t BH = (int64_t)p.B * p.H;
     double* qmean = ws;
     double* kmeanT = ws + BH * p.nB * p.d;
     {
-        dim3 grid((unsigned)(BH * p.nB), 2);
+        dim3 grid((unsigned)(BH * p.nB));
         const u32x4* q4 = reinterpret_cast<const u32x4*>(qr);
-        const u32x4* k4 = reinterpret_cast<const u32x4*>(kr);
-        if (p.d == 128)
-            hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, s, p, q4, k4, qmean, kmeanT);
-        else
-            hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, s, p, q4, k4, qmean, kmeanT);
+        const u32x4* k4 = reinterpret_cast<const u32x4*>(kt);
+        if (p.d == 128) {
+            hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, s, p, q4, qmean);
+            if (p.block == 128)
+                hipLaunchKernelGGL((pool_kt_kernel<128, 128>), grid, dim3(kPoolThreads), 0, s, p, k4, kmeanT);
+            else
+                hipLaunchKernelGGL((pool_kt_kernel<128, 64>), grid, dim3(kPoolThreads), 0, s, p, k4, kmeanT);
+        } else {
+            hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, s, p, q4, qmean);
+            if (p.block == 128)
+                hipLaunchKernelGGL((pool_kt_kernel<64, 128>), grid, dim3(kPoolThreads), 0, s, p, k4, kmeanT);
+            else
+                hipLaunchKernelGGL((pool_kt_kernel<64, 64>), grid, dim3(kPoolThreads), 0, s, p, k4, kmeanT);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    int R = kScoreLds / ((p.nB + p.d) * (int)sizeof(double));
+    // rows per workgroup: up to 8, as many as the score rows' LDS allows
+    int R = (kScoreLds - 8 * p.d * (int)sizeof(double)) / (p.nB * (int)sizeof(double));
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
     const int groups = (p.nB + R - 1) / R;
     dim3 grid((unsigned)(BH * groups));
-    const size_t lds = (size_t)R * (p.d + p.nB) * sizeof(double);
+    const size_t lds = (size_t)(8 * p.d + R * p.nB) * sizeof(double);
     const int nslot = (p.nB + 63) / 64;
 #define SVA_TOPK(DD, NS) \
     hipLaunchKernelGGL((topk_kernel<DD, NS>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
-    if (p.d == 128) {
-        if (nslot <= 16) SVA_TOPK(128, 16);
-        else if (nslot <= 32) SVA_TOPK(128, 32);
-        else SVA_TOPK(128, 64);
-    } else {
-        if (nslot <= 16) SVA_TOPK(64, 16);
-        else if (nslot <= 32) SVA_TOPK(64, 32);
-        else SVA_TOPK(64, 64);
-    }
+#define SVA_TOPK_D(DD)                                                                       \
+    do {                                                                                     \
+        if (nslot <= 4) SVA_TOPK(DD, 4);                                                     \
+        else if (nslot <= 8) SVA_TOPK(DD, 8);                                                \
+        else if (nslot <= 12) SVA_TOPK(DD, 12);                                              \
+        else if (nslot <= 16) SVA_TOPK(DD, 16);                                              \
+        else if (nslot <= 32) SVA_TOPK(DD, 32);                                              \
+        else SVA_TOPK(DD, 64);                                                               \
+    } while (0)
+    if (p.d == 128) SVA_TOPK_D(128);
+    else SVA_TOPK_D(64);
+#undef SVA_TOPK_D
 #undef SVA_TOPK
     return hipGetLastError();
 }

@@ -7,6 +7,26 @@
 
 namespace sva {
 
+// Exact unsigned division by a plan constant: for 0 <= x < 2^31,
+// x / d == (x · m) >> s with l = ceil(log2 d), s = 31 + l and
+// m = ceil(2^s / d) < 2^32 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, theorem 4.2 with N = 31).
+struct FastDiv {
+    uint32_t m;
+    int s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t two_s = 1ull << (31 + l);
+    return FastDiv{(uint32_t)((two_s + d - 1) / d), 31 + l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t x, FastDiv f) {
+    return (uint32_t)(((uint64_t)x * f.m) >> f.s);
+}
+
 // Everything a kernel needs to know about a plan, passed by value.
 struct DevPlan {
     int B, H, d, block;
@@ -27,6 +47,8 @@ struct DevPlan {
     const int32_t* row_ptr;    // [nB+1]
     int64_t nnz_per_head;
     int max_row_len;
+    // divisions of (token, head) row indices, all below 2^31
+    FastDiv div_H, div_N, div_HW, div_W;
 };
 
 hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
@@ -36,8 +58,9 @@ hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* 
 hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
                           hipStream_t s);
 
+// qr: Q' in tile order; kt: K' as K tiles.
 // ws: [B,H,nB,d] q means followed by [B,H,d,nB] k means (float64)
-hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kr, double* ws,
+hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s);
 
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,

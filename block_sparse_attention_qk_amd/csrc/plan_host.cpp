@@ -74,8 +74,8 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     const int64_t nB = Np / d.block;
     if (nB > 4096)
         return fail(err, SVA_ERR_INVALID_ARG, "more than 4096 blocks per head");
-    if ((int64_t)d.B * d.H * Np * d.d >= ((int64_t)1 << 40))
-        return fail(err, SVA_ERR_INVALID_ARG, "tensor too large");
+    if ((int64_t)d.B * d.H * Np >= ((int64_t)1 << 31))
+        return fail(err, SVA_ERR_INVALID_ARG, "tensor too large (2^31 or more rows of d)");
 
     p.desc = d;
     sva_plan_info& I = p.info;

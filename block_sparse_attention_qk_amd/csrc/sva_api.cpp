@@ -154,6 +154,10 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     }
     d.nnz_per_head = I.nnz_per_head;
     d.max_row_len = I.max_row_len;
+    d.div_H = sva::make_fastdiv((uint32_t)ds.H);
+    d.div_N = sva::make_fastdiv((uint32_t)I.N);
+    d.div_HW = sva::make_fastdiv((uint32_t)(ds.Hh * ds.W));
+    d.div_W = sva::make_fastdiv((uint32_t)ds.W);
     *out = plan;
     return SVA_OK;
 }
@@ -213,19 +217,19 @@ int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* s
     return SVA_OK;
 }
 
-int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r, void* workspace,
+int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t, void* workspace,
                       size_t workspace_bytes, int32_t* col, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
     if (plan->host.info.dense) return SVA_OK;
-    if (!q_r || !k_r || !col || !workspace)
-        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_r, workspace and col must be non-NULL");
-    if (!sva::aligned16(q_r) || !sva::aligned16(k_r) || !sva::aligned16(workspace) ||
+    if (!q_r || !k_t || !col || !workspace)
+        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, workspace and col must be non-NULL");
+    if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(workspace) ||
         ((uintptr_t)col & 3u))
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
     if (workspace_bytes < plan->host.info.select_workspace_bytes)
         return set_err(SVA_ERR_WORKSPACE, "workspace smaller than select_workspace_bytes");
     hipError_t e = sva::launch_select(plan->dev, static_cast<const uint16_t*>(q_r),
-                                      static_cast<const uint16_t*>(k_r),
+                                      static_cast<const uint16_t*>(k_t),
                                       static_cast<double*>(workspace), col,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "select launch");

@@ -172,15 +172,16 @@ int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k,
  * them.  `in` and `out` must not overlap. */
 int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* stream);
 
-/* Block selection.  q_r, k_r: tile order [B, H, Np, d] (outputs of the
- * prologue after SVA_FORWARD).  For every (b, h, query block qb):
- * score(kb) = mean(q_r rows of qb) · mean(k_r rows of kb), means over valid
- * tokens; keep the forced blocks and then the best-scored blocks (score
- * descending, lower block index first on equal scores) until the row holds
- * row_ptr[qb+1] - row_ptr[qb] blocks.  Writes `col` [nnz] int32, each row
- * in ascending block order.  `workspace` (device, info.select_workspace_bytes)
- * holds the block means.  Nothing to do for a dense plan (col may be NULL). */
-int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_r,
+/* Block selection.  q_r: tile order [B, H, Np, d] (SVA_FORWARD of Q');
+ * k_t: K tiles (SVA_FORWARD_KT of K', the same buffer sva_attention reads).
+ * For every (b, h, query block qb): score(kb) = mean(Q' rows of qb) ·
+ * mean(K' rows of kb), means over valid tokens; keep the forced blocks and
+ * then the best-scored blocks (score descending, lower block index first on
+ * equal scores) until the row holds row_ptr[qb+1] - row_ptr[qb] blocks.
+ * Writes `col` [nnz] int32, each row in ascending block order.  `workspace`
+ * (device, info.select_workspace_bytes) holds the block means.  Nothing to
+ * do for a dense plan (col may be NULL). */
+int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t,
                       void* workspace, size_t workspace_bytes, int32_t* col,
                       void* stream);
 

@@ -160,11 +160,11 @@ def test_select_parity(name):
     wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
     run = GpuRun(wl, q, k, v, wq, wk)
     qr = np.zeros((wl.B, wl.H, g.Np, g.d), np.uint16)
-    kr = np.zeros_like(qr)
+    kt = np.zeros((wl.B, wl.H, g.nB, g.block // 32, g.d // 16, 64, 8), np.uint16)
     for (b, h), r in ref.items():
         qr[b, h] = O.f64_to_bf16_bits(r["qr"])
-        kr[b, h] = O.f64_to_bf16_bits(r["kr"])
-    S.sva_select_blocks(run.plan, dev(qr), dev(kr), run.buf.ws, run.buf.col)
+        kt[b, h] = _kt_from_kr(O.f64_to_bf16_bits(r["kr"]), g)
+    S.sva_select_blocks(run.plan, dev(qr), dev(kt), run.buf.ws, run.buf.col)
     torch.cuda.synchronize()
     col = run.buf.col.cpu().numpy()
     _, row_ptr, _ = run.plan.host_tables()
@@ -262,7 +262,7 @@ def test_binding_rejects_bad_tensors():
         S.sva_reorder(plan, buf.qn.cpu(), buf.q_r, S.SVA_FORWARD)
     small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(S.SvaError) as e:
-        S.sva_select_blocks(plan, buf.q_r, buf.k_r, small_ws, buf.col)
+        S.sva_select_blocks(plan, buf.q_r, buf.k_t, small_ws, buf.col)
     assert e.value.status == S.SVA_ERR_WORKSPACE
 
 
@@ -329,8 +329,6 @@ def test_full_workload_sampled(name):
         kr_g = want.copy()
         if not np.array_equal(kt_g, _kt_from_kr(want, g)):
             fails.append(("reorder k tiles", h))
-        if col is not None and not np.array_equal(host(run.buf.k_r[0, h]), want):
-            fails.append(("reorder k", h))
         want[perm] = v[0, :, h]
         if not np.array_equal(vt_g, _vt_from_vr(want, g)):
             fails.append(("reorder v tiles", h))
