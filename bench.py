@@ -171,7 +171,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, d, b),
         },
         "stages_ms": {n: round(t, 4) for n, t in stage.items()},
         "stages_hbm_gbs": {n: round(t, 1) for n, t in stage_gbs.items()},
@@ -182,6 +182,25 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, q, k, v, wq, wk, info, args.cpu_heads, ms_step)
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload, d, b):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
+    None when there is none for this workload or the attention source has
+    changed since the counters were taken."""
+    from block_sparse_attention_qk_amd import profile_traffic as PT
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        res = json.load(f)
+    src = "k_attention.hip"
+    if res.get("sources_sha256", {}).get(src) != PT.source_hashes().get(src):
+        return None
+    name = f"attn_kernel<{d}, {b}, false>"
+    e = res.get("kernels", {}).get(name) or res.get("kernels", {}).get(f"attn_kernel<{d}, {b}, true>")
+    return None if e is None else round(e["traffic_bytes"], 0)
 
 
 def cpu_baseline(wl, q, k, v, wq, wk, info, heads, gpu_ms):
