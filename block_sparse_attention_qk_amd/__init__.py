@@ -154,7 +154,8 @@ def sva_plan_host_tables(desc: sva_plan_desc, forced: bool = False):
 def desc_for(wl) -> sva_plan_desc:
     """Plan description of a workload from ``inputs.WORKLOADS``."""
     return sva_plan_desc_init(wl.B, wl.H, wl.T, wl.Hh, wl.W, wl.d, wl.block, wl.sparsity,
-                              wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+                              wl.flags, tile=wl.tile, n_extra=wl.n_extra,
+                              rope_split=getattr(wl, "rope_split", (0, 0, 0)))
 
 
 # --------------------------------------------------------------------------

@@ -49,6 +49,7 @@ class Workload:
     n_extra: int = 0
     temperature: bool = False
     seed_base: int = 0
+    rope_split: tuple = (0, 0, 0)   # t/h/w RoPE channels; zeros = the plan's default
 
     @property
     def n_video(self) -> int:
@@ -170,7 +171,8 @@ def norm_weights(wl: Workload):
 
 def custom(name: str, B: int, H: int, T: int, Hh: int, W: int, d: int, block: int,
            sparsity: float, flags: int = 0, tile=(0, 0, 0), n_extra: int = 0,
-           temperature: bool = False, seed_base: int = 9000) -> Workload:
+           temperature: bool = False, seed_base: int = 9000,
+           rope_split=(0, 0, 0)) -> Workload:
     """An ad-hoc workload (tests use these for small ragged shapes)."""
     return Workload(name, B, H, T, Hh, W, d, block, sparsity, flags, tuple(tile),
-                    n_extra, temperature, seed_base)
+                    n_extra, temperature, seed_base, tuple(rope_split))

@@ -42,6 +42,11 @@ SMALL = {
     "dense128": I.custom("dense128", 1, 2, 5, 13, 17, 128, 128, 0.0, seed_base=9500),
     "denseflag64": I.custom("denseflag64", 1, 2, 3, 9, 20, 64, 64, 0.8, flags=I.DENSE,
                             tile=(1, 4, 16), seed_base=9600),
+    # partial RoPE as in the packed video + audio model: 96 of 128 channels
+    # rotated (32 per axis), extra tokens packed after the video
+    "partial96": I.custom("partial96", 1, 2, 4, 8, 24, 128, 128, 0.5,
+                          flags=I.KEEP_SAME_FRAME, n_extra=128, seed_base=9700,
+                          rope_split=(32, 32, 32)),
 }
 
 
