@@ -18,10 +18,13 @@ notes and repeated next to each function):
    tail to a multiple of the block size; extra (audio/text) tokens follow.
 3. Mean pooling of Q' and K' per block ("SubBlock 稀疏注意力如何工作": a
    lightweight pooling step scores key blocks per query block and head).
-4. Block scores q̄·k̄, forced blocks, and top-k key blocks per (query block,
-   head) at keep ratio 1 - sparsity (same section: sparsity is the fraction of
-   key blocks dropped, ranking is independent per query block and head, and the
-   kept indices are handed to the block-sparse kernel).
+4. Block scores, forced blocks, and top-k key blocks per (query block, head)
+   at keep ratio 1 - sparsity (same section: sparsity is the fraction of key
+   blocks dropped, ranking is independent per query block and head, and the
+   kept indices are handed to the block-sparse kernel).  Two scorers: the mean
+   scorer q̄·k̄, and the SubBlock scorer of the same section (sub-block means
+   combined by log-sum-exp into an estimate of each key block's unnormalised
+   softmax mass), optionally with the budget rounded to multiples of 8.
 5. Exact softmax attention of each query over the valid keys of its kept
    blocks, non-causal (same section: the sparse path serves non-causal DiT
    attention and never builds the full attention matrix).  With every block
@@ -42,6 +45,8 @@ import numpy as np
 
 SVA_DENSE = 1
 SVA_KEEP_SAME_FRAME = 2
+SCORER_MEAN = 0
+SCORER_SUBBLOCK = 1
 
 
 # --------------------------------------------------------------------------
@@ -98,6 +103,9 @@ class Geometry:
     theta: float = 10000.0
     split: tuple = (0, 0, 0)
     eps: float = 1e-6
+    scorer: int = SCORER_MEAN
+    subblocks: int = 0          # sub-blocks per block (SubBlock scorer); 0 = 4
+    budget_multiple: int = 1    # round the budget up to a multiple of this
     # derived
     n_video: int = field(init=False)
     N: int = field(init=False)
@@ -121,27 +129,32 @@ class Geometry:
         self.Np = self.n_video_pad + self.n_extra
         self.nB = self.Np // b
         self.nB_video = self.n_video_pad // b
-        self.k = budget(self.nB, self.sparsity, self.flags)
+        if self.subblocks == 0:
+            self.subblocks = 4 if self.scorer == SCORER_SUBBLOCK else 1
+        self.k = budget(self.nB, self.sparsity, self.flags, self.budget_multiple)
 
     @property
     def dense(self) -> bool:
         return bool(self.flags & SVA_DENSE) or self.sparsity == 0.0
 
 
-def budget(nB: int, sparsity: float, flags: int = 0) -> int:
+def budget(nB: int, sparsity: float, flags: int = 0, multiple: int = 1) -> int:
     """Key blocks kept per query row.
 
     The benchmark page ("SubBlock 稀疏注意力如何工作") defines sparsity as the
     fraction of key blocks that may be dropped, so sparsity 0.75 keeps about a
     quarter.  Reading: keep ceil((1 - sparsity)·nB) blocks (the 1e-9 guards a
     product that lands a hair above an integer), at least one, at most all;
-    sparsity 0 or the dense flag keeps every block.  The page's rounding of
-    the budget to multiples of 8 blocks belongs to its SubBlock router and is
-    not part of this plain reading.
+    sparsity 0 or the dense flag keeps every block.  The same section says the
+    SubBlock router's budget is rounded in units of 8 blocks; with
+    ``multiple`` > 1 the budget is rounded up to a multiple of it (reading:
+    up, so at least the requested fraction is kept), then clamped to nB.
     """
     if (flags & SVA_DENSE) or sparsity == 0.0:
         return nB
     k = math.ceil((1.0 - sparsity) * nB - 1e-9)
+    if multiple > 1:
+        k = -(-k // multiple) * multiple
     return max(1, min(nB, k))
 
 
@@ -298,6 +311,54 @@ def pool_means(xr, geom: Geometry, valid=None):
     return s / valid[:, None]
 
 
+def subblock_counts(geom: Geometry, valid=None):
+    """Valid tokens of each sub-block: [nB, n].  A block of b tile-order
+    positions is split into n runs of b/n consecutive positions; its valid
+    tokens are the first ``valid`` positions."""
+    if valid is None:
+        valid, _, _, _ = block_meta(geom)
+    n = geom.subblocks
+    sb = geom.block // n
+    start = np.arange(n) * sb
+    return np.clip(np.asarray(valid)[:, None] - start[None, :], 0, sb)
+
+
+def subblock_means(xr, geom: Geometry, valid=None):
+    """Mean of every sub-block over its valid tokens: [Np, d] → [nB, n, d]
+    (zero for a sub-block without valid tokens)."""
+    cnt = subblock_counts(geom, valid)
+    n = geom.subblocks
+    x = np.asarray(xr, dtype=np.float64)
+    s = x.reshape(geom.nB, n, geom.block // n, geom.d).sum(axis=2)
+    return np.where(cnt[..., None] > 0, s / np.maximum(cnt, 1)[..., None], 0.0)
+
+
+def subblock_scores(qsub, ksub, geom: Geometry, valid=None):
+    """SubBlock block scores: [nB, nB].
+
+    The benchmark page ("SubBlock 稀疏注意力如何工作") splits every query and
+    key block into sub-blocks, pools them, and scores each key block for a
+    query block by a log-sum-exp estimate of its unnormalised softmax mass.
+    Reading: replace every query and key by the mean of its sub-block; the
+    mass of key block kb for the query rows of qb,
+        sum_{p in qb} sum_{j in kb} exp(q_p·k_j / sqrt(d)),
+    becomes
+        score = log sum_a sum_b c_a c_b exp(q̄_a·k̄_b / sqrt(d)),
+    with c the valid counts of the sub-blocks (empty sub-blocks drop out).
+    It is exact when every sub-block holds identical rows.
+    """
+    cnt = subblock_counts(geom, valid).astype(np.float64)
+    d = geom.d
+    q = np.asarray(qsub, np.float64)
+    k = np.asarray(ksub, np.float64)
+    with np.errstate(divide="ignore"):
+        lq = np.log(cnt)                 # -inf for empty sub-blocks
+    x = np.einsum("iad,jbd->ijab", q, k) / math.sqrt(d)
+    x = x + lq[:, None, :, None] + lq[None, :, None, :]
+    m = x.max(axis=(2, 3))
+    return m + np.log(np.exp(x - m[:, :, None, None]).sum(axis=(2, 3)))
+
+
 # --------------------------------------------------------------------------
 # Step 4: block scores and top-k selection
 # --------------------------------------------------------------------------
@@ -334,11 +395,18 @@ def row_lengths(geom: Geometry, meta=None):
 
 
 def select_blocks(qbar, kbar, geom: Geometry, meta=None):
-    """Kept key blocks of one (batch, head).
+    """Kept key blocks of one (batch, head) under the mean scorer.
 
-    qbar, kbar: [nB, d] block means.  Score s[qb, kb] = q̄_qb · k̄_kb.  Each
-    row keeps its forced blocks plus the best remaining blocks ordered by
-    (score descending, block index ascending) until it holds
+    qbar, kbar: [nB, d] block means.  Score s[qb, kb] = q̄_qb · k̄_kb; the
+    selection is ``select_from_scores``.
+    """
+    scores = np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T
+    return select_from_scores(scores, geom, meta)
+
+
+def select_from_scores(scores, geom: Geometry, meta=None):
+    """Each row keeps its forced blocks plus the best remaining blocks
+    ordered by (score descending, block index ascending) until it holds
     ``row_lengths`` blocks.
 
     Returns (kept [nB, nB] bool, scores [nB, nB], thresh [nB], smax [nB]):
@@ -348,7 +416,7 @@ def select_blocks(qbar, kbar, geom: Geometry, meta=None):
     forced, dense_row = forced_blocks(geom, meta)
     nB = geom.nB
     lens = row_lengths(geom, meta)
-    scores = np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T
+    scores = np.asarray(scores, np.float64)
     kept = np.zeros((nB, nB), dtype=bool)
     thresh = np.full(nB, np.nan)
     smax = np.abs(scores).max(axis=1)
@@ -363,8 +431,8 @@ def select_blocks(qbar, kbar, geom: Geometry, meta=None):
         if need <= 0:
             continue
         cand = idx[~f]
-        s = scores[qb, cand]
-        order = np.lexsort((cand, -s))     # score desc, then index asc
+        sc = scores[qb, cand]
+        order = np.lexsort((cand, -sc))    # score desc, then index asc
         take = cand[order[:need]]
         kept[qb, take] = True
         thresh[qb] = scores[qb, take[-1]]
@@ -450,7 +518,12 @@ def run_head(q, k, v, wq, wk, geom: Geometry, qblocks=None, perm=None, meta=None
     vr[perm] = np.asarray(v, np.float64)
     qbar = pool_means(qr, geom, meta[0])
     kbar = pool_means(kr, geom, meta[0])
-    kept, scores, thresh, smax = select_blocks(qbar, kbar, geom, meta)
+    if geom.scorer == SCORER_SUBBLOCK:
+        scores = subblock_scores(subblock_means(qr, geom, meta[0]),
+                                 subblock_means(kr, geom, meta[0]), geom, meta[0])
+        kept, scores, thresh, smax = select_from_scores(scores, geom, meta)
+    else:
+        kept, scores, thresh, smax = select_blocks(qbar, kbar, geom, meta)
     o_r = block_attention(qr, kr, vr, kept, geom, meta, qblocks)
     return dict(qn=qn, kn=kn, qr=qr, kr=kr, vr=vr, qbar=qbar, kbar=kbar,
                 kept=kept, scores=scores, thresh=thresh, smax=smax,

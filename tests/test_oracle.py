@@ -324,6 +324,84 @@ def test_selection_properties():
         prev = ks
 
 
+def test_budget_multiple():
+    # hand-worked: ceil((1 - s)·nB) rounded up to a multiple of 8, clamped to nB
+    assert O.budget(591, 0.75, 0, 8) == 152      # 148 -> 152
+    assert O.budget(591, 0.80, 0, 8) == 120      # ceil(118.2) = 119 -> 120
+    assert O.budget(16, 0.5, 0, 8) == 8          # 8 stays 8
+    assert O.budget(10, 0.9, 0, 8) == 8          # 1 -> 8
+    assert O.budget(5, 0.5, 0, 8) == 5           # 3 -> 8 -> clamped to 5
+    assert O.budget(591, 0.75, 0, 1) == O.budget(591, 0.75)
+    assert O.budget(40, 0.5, O.SVA_DENSE, 8) == 40
+
+
+# ---------------------------------------------------------------- SubBlock scorer
+
+def _sub_geom(n=4, n_extra=64, W=10, block=64):
+    # 2×6×10 = 120 video tokens: block 1 is ragged (56 valid of 64), so its
+    # sub-blocks hold 16, 16, 16 and 8 tokens; one extra-token block follows
+    return O.Geometry(B=1, H=1, T=2, Hh=6, W=W, d=32, block=block, sparsity=0.5,
+                      tile=(1, 6, 10), n_extra=n_extra, scorer=O.SCORER_SUBBLOCK, subblocks=n)
+
+
+def check_subblock_exact():
+    """Rows constant within each sub-block: the SubBlock estimate is the
+    exact unnormalised softmax mass of each block pair (brute force)."""
+    g = _sub_geom()
+    valid, _, _, _ = O.block_meta(g)
+    cnt = O.subblock_counts(g, valid)
+    assert cnt.tolist()[:2] == [[16, 16, 16, 16], [16, 16, 16, 8]]
+    rng = np.random.default_rng(21)
+    n, sb = g.subblocks, g.block // g.subblocks
+    def field():
+        x = np.zeros((g.Np, g.d))
+        for kb in range(g.nB):
+            for a in range(n):
+                c = cnt[kb, a]
+                if c:
+                    x[kb * g.block + a * sb: kb * g.block + a * sb + c] = rng.standard_normal(g.d)
+        return x
+    qr, kr = field(), field()
+    sc = O.subblock_scores(O.subblock_means(qr, g, valid), O.subblock_means(kr, g, valid), g, valid)
+    for qb in range(g.nB):
+        for kb in range(g.nB):
+            mass = 0.0
+            for p in range(qb * g.block, qb * g.block + valid[qb]):
+                for j in range(kb * g.block, kb * g.block + valid[kb]):
+                    mass += math.exp(sum(qr[p, i] * kr[j, i] for i in range(g.d)) / math.sqrt(g.d))
+            assert abs(sc[qb, kb] - math.log(mass)) <= 1e-12 * max(1.0, abs(math.log(mass))), (qb, kb)
+
+
+def test_subblock_scores_exact_on_constant_subblocks():
+    check_subblock_exact()
+
+
+def test_subblock_one_subblock_ranks_like_mean():
+    # every block full and one sub-block per block: the estimate is
+    # log(b²) + q̄·k̄/sqrt(d), a monotone map of the mean scorer's q̄·k̄
+    g1 = O.Geometry(B=1, H=1, T=4, Hh=8, W=16, d=64, block=64, sparsity=0.75,
+                    tile=(2, 4, 8), scorer=O.SCORER_SUBBLOCK, subblocks=1)
+    gm = O.Geometry(B=1, H=1, T=4, Hh=8, W=16, d=64, block=64, sparsity=0.75, tile=(2, 4, 8))
+    rng = np.random.default_rng(22)
+    qr = rng.standard_normal((g1.Np, g1.d))
+    kr = rng.standard_normal((g1.Np, g1.d))
+    sc = O.subblock_scores(O.subblock_means(qr, g1), O.subblock_means(kr, g1), g1)
+    kept1 = O.select_from_scores(sc, g1)[0]
+    keptm = O.select_blocks(O.pool_means(qr, gm), O.pool_means(kr, gm), gm)[0]
+    assert np.array_equal(kept1, keptm)
+    np.testing.assert_allclose(
+        sc, np.log(64.0 * 64.0) + O.pool_means(qr, gm) @ O.pool_means(kr, gm).T / 8.0, rtol=1e-13)
+
+
+def test_subblock_scores_stay_finite_for_large_logits():
+    g = _sub_geom()
+    rng = np.random.default_rng(23)
+    qr = rng.standard_normal((g.Np, g.d)) * 300.0
+    kr = rng.standard_normal((g.Np, g.d)) * 300.0
+    sc = O.subblock_scores(O.subblock_means(qr, g), O.subblock_means(kr, g), g)
+    assert np.all(np.isfinite(sc))
+
+
 def test_selection_ties_take_lowest_index():
     g, _, _ = _sel_setup()
     z = np.zeros((g.nB, g.d))
@@ -539,3 +617,20 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "block_attention", bad_attn2)
     assert _fails(check_sparse_attention_masked_sdpa)
     monkeypatch.setattr(O, "block_attention", orig_attn)
+    # 9. SubBlock estimate without the sub-block counts
+    orig_cnt = O.subblock_counts
+    monkeypatch.setattr(O, "subblock_counts",
+                        lambda g, valid=None: np.minimum(orig_cnt(g, valid), 1))
+    assert _fails(check_subblock_exact)
+    monkeypatch.setattr(O, "subblock_counts", orig_cnt)
+    # 10. SubBlock estimate with the max instead of the sum over sub-block pairs
+    orig_sub = O.subblock_scores
+    def bad_sub(qs, ks, g, valid=None):
+        cnt = O.subblock_counts(g, valid).astype(float)
+        with np.errstate(divide="ignore"):
+            lq = np.log(cnt)
+        x = np.einsum("iad,jbd->ijab", qs, ks) / math.sqrt(g.d)
+        return (x + lq[:, None, :, None] + lq[None, :, None, :]).max(axis=(2, 3))
+    monkeypatch.setattr(O, "subblock_scores", bad_sub)
+    assert _fails(check_subblock_exact)
+    monkeypatch.setattr(O, "subblock_scores", orig_sub)
