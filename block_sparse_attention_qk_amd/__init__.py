@@ -28,6 +28,9 @@ SVA_ERR_HIP = -4
 SVA_DENSE = 1
 SVA_KEEP_SAME_FRAME = 2
 
+SVA_SCORER_MEAN = 0
+SVA_SCORER_SUBBLOCK = 1
+
 SVA_FORWARD = 0
 SVA_INVERSE = 1
 SVA_FORWARD_VT = 2
@@ -52,6 +55,8 @@ class sva_plan_desc(ctypes.Structure):
         ("rope_theta", ctypes.c_double),
         ("rope_split", ctypes.c_int * 3),
         ("eps", ctypes.c_double),
+        ("scorer", ctypes.c_int), ("subblocks", ctypes.c_int),
+        ("budget_multiple", ctypes.c_int),
     ]
 
 
@@ -66,6 +71,8 @@ class sva_plan_info(ctypes.Structure):
         ("dense", ctypes.c_int32),
         ("tile", ctypes.c_int32 * 3),
         ("rope_split", ctypes.c_int32 * 3),
+        ("scorer", ctypes.c_int32), ("subblocks", ctypes.c_int32),
+        ("budget_multiple", ctypes.c_int32),
     ]
 
 
@@ -121,7 +128,8 @@ def _check(status: int) -> None:
 # --------------------------------------------------------------------------
 
 def sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, flags=0, tile=(0, 0, 0),
-                       n_extra=0, rope_theta=0.0, rope_split=(0, 0, 0), eps=0.0) -> sva_plan_desc:
+                       n_extra=0, rope_theta=0.0, rope_split=(0, 0, 0), eps=0.0,
+                       scorer=SVA_SCORER_MEAN, subblocks=0, budget_multiple=0) -> sva_plan_desc:
     desc = sva_plan_desc()
     _check(lib().sva_plan_desc_init(ctypes.byref(desc), B, H, T, Hh, W, d, block,
                                     float(sparsity), flags))
@@ -130,6 +138,9 @@ def sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, flags=0, tile=(0, 0, 
     desc.rope_theta = rope_theta
     desc.rope_split[:] = list(rope_split)
     desc.eps = eps
+    desc.scorer = scorer
+    desc.subblocks = subblocks
+    desc.budget_multiple = budget_multiple
     return desc
 
 
@@ -155,7 +166,10 @@ def desc_for(wl) -> sva_plan_desc:
     """Plan description of a workload from ``inputs.WORKLOADS``."""
     return sva_plan_desc_init(wl.B, wl.H, wl.T, wl.Hh, wl.W, wl.d, wl.block, wl.sparsity,
                               wl.flags, tile=wl.tile, n_extra=wl.n_extra,
-                              rope_split=getattr(wl, "rope_split", (0, 0, 0)))
+                              rope_split=getattr(wl, "rope_split", (0, 0, 0)),
+                              scorer=getattr(wl, "scorer", SVA_SCORER_MEAN),
+                              subblocks=getattr(wl, "subblocks", 0),
+                              budget_multiple=getattr(wl, "budget_multiple", 0))
 
 
 # --------------------------------------------------------------------------

@@ -6,6 +6,11 @@
 // dropped) and their indices go to the block-sparse kernel; rows are ranked
 // independently per query block and head.  The score here is the plain
 // reading of "mean-pooled Q and K": s(qb, kb) = mean(Q' of qb) · mean(K' of kb).
+// The SubBlock scorer of the same section splits each block into runs of
+// consecutive tokens, pools each run, and scores a key block by
+//   log sum_a sum_b c_a c_b exp(qbar_a · kbar_b / sqrt(d))
+// over the runs' valid counts c, an estimate of the key block's
+// unnormalised softmax mass for the query block.
 //
 // Two kernels:
 //  pool   one workgroup per (b, h, block) and tensor: float64 sums of the
@@ -39,13 +44,15 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const u32
     __shared__ double part[RG][D];
     const int kb = blockIdx.x % p.nB;
     const int64_t bh = blockIdx.x / p.nB;
+    const int sb = p.block / p.nsub;         // rows per run
+    const int s0 = blockIdx.y * sb;          // first row of this run
     const u32x4* src = qr + (bh * p.Np + (int64_t)kb * p.block) * LPR;
     const int dc = threadIdx.x % LPR;
     const int rg = threadIdx.x / LPR;
-    const int valid = p.blk_valid[kb];
+    const int valid = min(max(p.blk_valid[kb] - s0, 0), sb);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int r = rg; r < valid; r += RG) {
-        const u32x4 v = src[(int64_t)r * LPR + dc];
+        const u32x4 v = src[(int64_t)(s0 + r) * LPR + dc];
         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -60,37 +67,39 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevPlan p, const u32
         double s = 0.0;
 #pragma unroll 4
         for (int g = 0; g < RG; ++g) s += part[g][threadIdx.x];
-        qmean[(bh * p.nB + kb) * D + threadIdx.x] = s / (double)valid;
+        qmean[((bh * p.nB + kb) * p.nsub + blockIdx.y) * D + threadIdx.x] =
+            valid > 0 ? s / (double)valid : 0.0;
     }
 }
 
 // K means from K tiles: token r = 32g + j of a block sits in entry
 // g·4D + c·32 + j of the block's tile for 8-channel chunk c (channels 8c ..
-// 8c+7).  Thread (j, q) sums chunks q, q + 8, ... over the groups; the 32
-// partial sums of a chunk are added through LDS.
+// 8c+7).  One workgroup per (block, run); thread (j, q) sums chunks q, q + 8,
+// ... over the run's tokens; the 32 partial sums of a chunk are added
+// through LDS.  Output transposed: [B, H, d, nB·nsub].
 template <int D, int BLK>
 __global__ __launch_bounds__(kPoolThreads) void pool_kt_kernel(DevPlan p, const u32x4* kt,
                                                                double* kmeanT) {
     constexpr int NCH = D / 8;                 // 8-channel chunks
     constexpr int CPT = NCH / 8;               // chunks per thread
-    constexpr int NG = BLK / 32;               // 32-token groups
     __shared__ double part[32][D + 1];
     const int kb = blockIdx.x % p.nB;
     const int64_t bh = blockIdx.x / p.nB;
+    const int sb = BLK / p.nsub;               // tokens per run
+    const int s0 = blockIdx.y * sb;
     const u32x4* src = kt + (bh * p.nB + kb) * (int64_t)(BLK * NCH);
     const int j = threadIdx.x % 32, q = threadIdx.x / 32;
-    const int valid = p.blk_valid[kb];
+    const int valid = min(max(p.blk_valid[kb] - s0, 0), sb);
     double acc[CPT][8];
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.0;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        if (g * 32 + j >= valid) break;
+    for (int r = j; r < valid; r += 32) {
+        const int tok = s0 + r;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const u32x4 v = src[g * 4 * D + (q + 8 * i) * 32 + j];
+            const u32x4 v = src[(tok >> 5) * 4 * D + (q + 8 * i) * 32 + (tok & 31)];
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -108,7 +117,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kt_kernel(DevPlan p, const 
         double s = 0.0;
 #pragma unroll 8
         for (int jj = 0; jj < 32; ++jj) s += part[jj][threadIdx.x];
-        kmeanT[(bh * D + threadIdx.x) * p.nB + kb] = s / (double)valid;
+        kmeanT[(bh * D + threadIdx.x) * ((int64_t)p.nB * p.nsub) + (int64_t)kb * p.nsub + blockIdx.y] =
+            valid > 0 ? s / (double)valid : 0.0;
     }
 }
 
@@ -139,15 +149,23 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
     return v;
 }
 
-template <int D, int NSLOT>
+// log of the valid count of run a of block b (-inf for an empty run)
+__device__ __forceinline__ double log_count(const DevPlan& p, int b, int a) {
+    const int sb = p.block / p.nsub;
+    const int c = min(max(p.blk_valid[b] - a * sb, 0), sb);
+    return c > 0 ? log((double)c) : -INFINITY;
+}
+
+template <int D, int NSLOT, int NSUB>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const double* qmean,
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
     constexpr int RT = 8;              // rows computed per pass over the key means
     constexpr int DB = 16;             // key-mean loads in flight per thread
+    constexpr int QW = RT * NSUB;      // query runs held per pass
     extern __shared__ double smem[];
-    double* qs = smem;                 // [D][RT], rows past nrows zero
-    double* sc = smem + RT * D;        // [R][nB]
+    double* qs = smem;                 // [D][QW], rows past nrows zero
+    double* sc = smem + QW * D;        // [R][nB]
     const int nB = p.nB;
     const int groups = (nB + R - 1) / R;
     const int g = blockIdx.x % groups;
@@ -155,37 +173,101 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     const int qb0 = g * R;
     const int nrows = min(R, nB - qb0);
 
-    for (int i = threadIdx.x; i < RT * D; i += kTopkThreads) {
-        const int dd = i / RT, r = i % RT;
-        qs[i] = r < nrows ? qmean[(bh * nB + qb0 + r) * D + dd] : 0.0;
+    for (int i = threadIdx.x; i < QW * D; i += kTopkThreads) {
+        const int dd = i / QW, ra = i % QW;
+        qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
     }
     __syncthreads();
 
-    // scores: thread per key block, all RT rows at once; each score is the
-    // sequential fma chain over the channels
-    const double* kt = kmeanT + bh * D * (int64_t)nB;
-    for (int kb = threadIdx.x; kb < nB; kb += kTopkThreads) {
-        double acc[RT];
+    const double* kt = kmeanT + bh * D * (int64_t)nB * NSUB;
+    if (NSUB == 1 && p.scorer == 0) {
+        // mean scorer: thread per key block, all RT rows at once; each score
+        // is the sequential fma chain over the channels
+        for (int kb = threadIdx.x; kb < nB; kb += kTopkThreads) {
+            double acc[RT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r] = 0.0;
-        for (int d0 = 0; d0 < D; d0 += DB) {
-            double kv[DB];
+            for (int r = 0; r < RT; ++r) acc[r] = 0.0;
+            for (int d0 = 0; d0 < D; d0 += DB) {
+                double kv[DB];
 #pragma unroll
-            for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nB + kb];
+                for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nB + kb];
 #pragma unroll
-            for (int i = 0; i < DB; ++i) {
-                const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * RT);
+                for (int i = 0; i < DB; ++i) {
+                    const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * RT);
 #pragma unroll
-                for (int r2 = 0; r2 < RT / 2; ++r2) {
-                    const double2 qq = q2[r2];
-                    acc[2 * r2] = fma(qq.x, kv[i], acc[2 * r2]);
-                    acc[2 * r2 + 1] = fma(qq.y, kv[i], acc[2 * r2 + 1]);
+                    for (int r2 = 0; r2 < RT / 2; ++r2) {
+                        const double2 qq = q2[r2];
+                        acc[2 * r2] = fma(qq.x, kv[i], acc[2 * r2]);
+                        acc[2 * r2 + 1] = fma(qq.y, kv[i], acc[2 * r2 + 1]);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
-            if (r < nrows) sc[r * nB + kb] = acc[r];
+            for (int r = 0; r < RT; ++r)
+                if (r < nrows) sc[r * nB + kb] = acc[r];
+        }
+    } else {
+        // SubBlock scorer: thread per key run (kb, b), the NSUB runs of a key
+        // block in adjacent lanes.  Dot products with every query run of the
+        // RT rows, then per row the log-sum-exp over query runs (in the
+        // thread) and key runs (across the NSUB lanes).
+        const double inv_sqrt_d = 1.0 / sqrt((double)D);
+        const int nks = nB * NSUB;
+        const int iters = (nks + kTopkThreads - 1) / kTopkThreads;
+        for (int it = 0; it < iters; ++it) {
+            const int ks = it * kTopkThreads + threadIdx.x;
+            const bool act = ks < nks;
+            const int kcol = act ? ks : nks - 1;
+            double acc[QW];
+#pragma unroll
+            for (int r = 0; r < QW; ++r) acc[r] = 0.0;
+            for (int d0 = 0; d0 < D; d0 += DB) {
+                double kv[DB];
+#pragma unroll
+                for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nks + kcol];
+#pragma unroll
+                for (int i = 0; i < DB; ++i) {
+                    const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * QW);
+#pragma unroll
+                    for (int r2 = 0; r2 < QW / 2; ++r2) {
+                        const double2 qq = q2[r2];
+                        acc[2 * r2] = fma(qq.x, kv[i], acc[2 * r2]);
+                        acc[2 * r2 + 1] = fma(qq.y, kv[i], acc[2 * r2 + 1]);
+                    }
+                }
+            }
+            const int kb = kcol / NSUB, b = kcol % NSUB;
+            const double lk = log_count(p, kb, b);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int qb = qb0 + min(r, nrows - 1);
+                double m = -INFINITY;
+                double x[NSUB];
+#pragma unroll
+                for (int a = 0; a < NSUB; ++a) {
+                    x[a] = acc[r * NSUB + a] * inv_sqrt_d + log_count(p, qb, a) + lk;
+                    m = fmax(m, x[a]);
+                }
+                double sum = 0.0;
+                if (m > -INFINITY) {
+#pragma unroll
+                    for (int a = 0; a < NSUB; ++a) sum += exp(x[a] - m);
+                }
+                // combine the NSUB key runs of this key block (adjacent lanes)
+#pragma unroll
+                for (int off = 1; off < NSUB; off <<= 1) {
+                    const double mo = __shfl_xor(m, off, 64);
+                    const double so = __shfl_xor(sum, off, 64);
+                    const double mn = fmax(m, mo);
+                    if (mn > -INFINITY) {
+                        sum = (m > -INFINITY ? sum * exp(m - mn) : 0.0) +
+                              (mo > -INFINITY ? so * exp(mo - mn) : 0.0);
+                        m = mn;
+                    }
+                }
+                if (act && b == 0 && r < nrows) sc[r * nB + kb] = m + log(sum);
+            }
+        }
     }
     __syncthreads();
 
@@ -269,10 +351,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
 hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s) {
     const int64_t BH = (int64_t)p.B * p.H;
-    double* qmean = ws;
-    double* kmeanT = ws + BH * p.nB * p.d;
+    double* qmean = ws;                                  // [B,H,nB,nsub,d]
+    double* kmeanT = ws + BH * p.nB * p.nsub * p.d;      // [B,H,d,nB·nsub]
     {
-        dim3 grid((unsigned)(BH * p.nB));
+        dim3 grid((unsigned)(BH * p.nB), (unsigned)p.nsub);
         const u32x4* q4 = reinterpret_cast<const u32x4*>(qr);
         const u32x4* k4 = reinterpret_cast<const u32x4*>(kt);
         if (p.d == 128) {
@@ -292,26 +374,35 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
         if (e != hipSuccess) return e;
     }
     // rows per workgroup: up to 8, as many as the score rows' LDS allows
-    int R = (kScoreLds - 8 * p.d * (int)sizeof(double)) / (p.nB * (int)sizeof(double));
+    // next to the query runs (8 rows × nsub runs × d)
+    const int qbytes = 8 * p.nsub * p.d * (int)sizeof(double);
+    int R = (kScoreLds - qbytes) / (p.nB * (int)sizeof(double));
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
     const int groups = (p.nB + R - 1) / R;
     dim3 grid((unsigned)(BH * groups));
-    const size_t lds = (size_t)(8 * p.d + R * p.nB) * sizeof(double);
+    const size_t lds = (size_t)qbytes + (size_t)R * p.nB * sizeof(double);
     const int nslot = (p.nB + 63) / 64;
-#define SVA_TOPK(DD, NS) \
-    hipLaunchKernelGGL((topk_kernel<DD, NS>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
+#define SVA_TOPK(DD, NS, NSB) \
+    hipLaunchKernelGGL((topk_kernel<DD, NS, NSB>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
+#define SVA_TOPK_S(DD, NSB)                                                                  \
+    do {                                                                                     \
+        if (nslot <= 4) SVA_TOPK(DD, 4, NSB);                                                \
+        else if (nslot <= 8) SVA_TOPK(DD, 8, NSB);                                           \
+        else if (nslot <= 12) SVA_TOPK(DD, 12, NSB);                                         \
+        else if (nslot <= 16) SVA_TOPK(DD, 16, NSB);                                         \
+        else if (nslot <= 32) SVA_TOPK(DD, 32, NSB);                                         \
+        else SVA_TOPK(DD, 64, NSB);                                                          \
+    } while (0)
 #define SVA_TOPK_D(DD)                                                                       \
     do {                                                                                     \
-        if (nslot <= 4) SVA_TOPK(DD, 4);                                                     \
-        else if (nslot <= 8) SVA_TOPK(DD, 8);                                                \
-        else if (nslot <= 12) SVA_TOPK(DD, 12);                                              \
-        else if (nslot <= 16) SVA_TOPK(DD, 16);                                              \
-        else if (nslot <= 32) SVA_TOPK(DD, 32);                                              \
-        else SVA_TOPK(DD, 64);                                                               \
+        if (p.nsub == 1) SVA_TOPK_S(DD, 1);                                                  \
+        else if (p.nsub == 2) SVA_TOPK_S(DD, 2);                                             \
+        else SVA_TOPK_S(DD, 4);                                                              \
     } while (0)
     if (p.d == 128) SVA_TOPK_D(128);
     else SVA_TOPK_D(64);
 #undef SVA_TOPK_D
+#undef SVA_TOPK_S
 #undef SVA_TOPK
     return hipGetLastError();
 }

@@ -35,6 +35,8 @@ struct DevPlan {
     int nB, nB_video, k;
     int dense;          // every block kept
     int same_frame;     // SVA_KEEP_SAME_FRAME
+    int scorer;         // SVA_SCORER_*
+    int nsub;           // runs per block (1 for the mean scorer)
     float eps;
     int rope_off[3];    // offsets (in cos/sin pairs) of the t, h, w tables
     int rope_half[3];   // rotated pairs per section

@@ -8,7 +8,9 @@
 //    the sequence is padded once at the tail to a multiple of the block;
 //  - the block budget follows the definition of sparsity as the fraction of
 //    key blocks dropped ("MiniMax-H3 在 8×H200 上基准测试", section
-//    "SubBlock 稀疏注意力如何工作"): k = ceil((1 - sparsity)·nB), at least 1;
+//    "SubBlock 稀疏注意力如何工作"): k = ceil((1 - sparsity)·nB), optionally
+//    rounded up to a multiple of budget_multiple (that section rounds the
+//    SubBlock router's budget in units of 8 blocks), clamped to [1, nB];
 //  - forced blocks (extra-token columns, same-frame blocks) count toward
 //    the budget, so a row keeps max(k, forced) blocks; extra-token rows are
 //    dense.  Row lengths therefore depend only on the geometry and the
@@ -63,6 +65,16 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     }
     if (split_sum > d.d)
         return fail(err, SVA_ERR_INVALID_ARG, "RoPE sections exceed the head dim");
+    if (d.scorer != SVA_SCORER_MEAN && d.scorer != SVA_SCORER_SUBBLOCK)
+        return fail(err, SVA_ERR_INVALID_ARG, "unknown scorer");
+    if (d.subblocks == 0) d.subblocks = d.scorer == SVA_SCORER_SUBBLOCK ? 4 : 1;
+    if (d.scorer == SVA_SCORER_MEAN && d.subblocks != 1)
+        return fail(err, SVA_ERR_INVALID_ARG, "the mean scorer has one run per block");
+    if (d.subblocks != 1 && d.subblocks != 2 && d.subblocks != 4)
+        return fail(err, SVA_ERR_UNSUPPORTED, "subblocks must be 1, 2 or 4");
+    if (d.budget_multiple == 0) d.budget_multiple = 1;
+    if (d.budget_multiple < 1)
+        return fail(err, SVA_ERR_INVALID_ARG, "budget_multiple must be >= 0");
     if (d.eps == 0.0) d.eps = 1e-6;
     if (!(d.eps > 0.0) || !std::isfinite(d.eps))
         return fail(err, SVA_ERR_INVALID_ARG, "eps must be > 0");
@@ -92,11 +104,16 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     } else {
         double kk = std::ceil((1.0 - d.sparsity) * (double)nB - 1e-9);
         int64_t k = (int64_t)kk;
+        if (d.budget_multiple > 1)
+            k = (k + d.budget_multiple - 1) / d.budget_multiple * d.budget_multiple;
         if (k < 1) k = 1;
         if (k > nB) k = nB;
         I.k = (int32_t)k;
     }
     I.tile[0] = d.tile_t; I.tile[1] = d.tile_h; I.tile[2] = d.tile_w;
+    I.scorer = d.scorer;
+    I.subblocks = d.subblocks;
+    I.budget_multiple = d.budget_multiple;
     for (int a = 0; a < 3; ++a) I.rope_split[a] = d.rope_split[a];
 
     // --- permutation ---
@@ -163,7 +180,8 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     I.nnz = I.nnz_per_head * d.B * d.H;
     // workspace: q block means [B,H,nB,d] and transposed k block means
     // [B,H,d,nB], float64
-    I.select_workspace_bytes = I.dense ? 0 : (size_t)2 * d.B * d.H * nB * d.d * sizeof(double);
+    I.select_workspace_bytes =
+        I.dense ? 0 : (size_t)2 * d.B * d.H * nB * d.subblocks * d.d * sizeof(double);
 
     // --- RoPE tables ---
     if (with_tables) {

@@ -147,6 +147,8 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.nB = I.nB; d.nB_video = I.nB_video; d.k = I.k;
     d.dense = I.dense;
     d.same_frame = (ds.flags & SVA_KEEP_SAME_FRAME) ? 1 : 0;
+    d.scorer = I.scorer;
+    d.nsub = I.subblocks;
     d.eps = (float)ds.eps;
     for (int a = 0; a < 3; ++a) {
         d.rope_off[a] = h.rope_off[a];

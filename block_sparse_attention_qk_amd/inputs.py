@@ -50,6 +50,9 @@ class Workload:
     temperature: bool = False
     seed_base: int = 0
     rope_split: tuple = (0, 0, 0)   # t/h/w RoPE channels; zeros = the plan's default
+    scorer: int = 0                 # 0 mean of each block, 1 SubBlock estimate
+    subblocks: int = 0              # runs per block for the SubBlock scorer (0 = 4)
+    budget_multiple: int = 0        # round the budget up to a multiple (0 = 1)
 
     @property
     def n_video(self) -> int:
@@ -81,6 +84,11 @@ WORKLOADS = {
     # packed video + 512 audio/text tokens (always-dense rows and columns)
     "packed768p_sp80": Workload("packed768p_sp80", 1, 48, 31, 48, 84, 128, 128, 0.80,
                                 tile=(2, 8, 8), n_extra=512, seed_base=4000),
+    # the 720p inputs under the SubBlock scorer (4 runs of 32 tokens per
+    # block, budget rounded up to a multiple of 8 blocks)
+    "wan720p_subblock": Workload("wan720p_subblock", 1, 40, 21, 45, 80, 128, 128, 0.75,
+                                 flags=KEEP_SAME_FRAME, tile=(2, 8, 8), temperature=True,
+                                 seed_base=2000, scorer=1, budget_multiple=8),
 }
 
 
@@ -172,7 +180,9 @@ def norm_weights(wl: Workload):
 def custom(name: str, B: int, H: int, T: int, Hh: int, W: int, d: int, block: int,
            sparsity: float, flags: int = 0, tile=(0, 0, 0), n_extra: int = 0,
            temperature: bool = False, seed_base: int = 9000,
-           rope_split=(0, 0, 0)) -> Workload:
+           rope_split=(0, 0, 0), scorer: int = 0, subblocks: int = 0,
+           budget_multiple: int = 0) -> Workload:
     """An ad-hoc workload (tests use these for small ragged shapes)."""
     return Workload(name, B, H, T, Hh, W, d, block, sparsity, flags, tuple(tile),
-                    n_extra, temperature, seed_base, tuple(rope_split))
+                    n_extra, temperature, seed_base, tuple(rope_split), scorer, subblocks,
+                    budget_multiple)

@@ -77,6 +77,15 @@ extern "C" {
 #define SVA_KEEP_SAME_FRAME  2u /* always keep key blocks whose frame range
                                    meets the query block's frame range */
 
+/* ---- block scorers (sva_plan_desc.scorer) ---- */
+#define SVA_SCORER_MEAN      0  /* score = mean(Q' of qb) · mean(K' of kb)     */
+#define SVA_SCORER_SUBBLOCK  1  /* "SubBlock 稀疏注意力如何工作": each block split
+                                   into `subblocks` runs of consecutive tile-order
+                                   tokens, pooled; score = log sum_a sum_b c_a c_b
+                                   exp(qbar_a · kbar_b / sqrt(d)) over the runs'
+                                   valid counts c (an estimate of the key block's
+                                   unnormalised softmax mass for the query block) */
+
 /* ---- sva_reorder directions ---- */
 #define SVA_FORWARD     0  /* raster [B,N,H,d] -> tile order [B,H,Np,d]      */
 #define SVA_INVERSE     1  /* tile order [B,H,Np,d] -> raster [B,N,H,d]      */
@@ -104,6 +113,13 @@ typedef struct {
                              sum <= d, channels past the sum are not rotated;
                              0,0,0 = 16/24/24 (d=64) or 44/42/42 (d=128)    */
     double eps;           /* RMSNorm epsilon; 0 = 1e-6                      */
+    int scorer;           /* SVA_SCORER_MEAN (0) or SVA_SCORER_SUBBLOCK     */
+    int subblocks;        /* SubBlock scorer: runs per block, 1, 2 or 4;
+                             0 = 4 (the pages' 16-token sub-blocks of
+                             64-token blocks); must be 0 or 1 for the mean
+                             scorer                                          */
+    int budget_multiple;  /* round the budget k up to a multiple of this
+                             (the pages' SubBlock router uses 8); 0 = 1     */
 } sva_plan_desc;
 
 /* Sizes derived from a description. */
@@ -114,8 +130,9 @@ typedef struct {
     int64_t Np;           /* n_video_pad + n_extra (tile-ordered rows)      */
     int32_t nB;           /* Np / block                                     */
     int32_t nB_video;     /* n_video_pad / block                            */
-    int32_t k;            /* key-block budget per row: ceil((1-sparsity)·nB),
-                             at least 1; nB when dense                      */
+    int32_t k;            /* key-block budget per row: ceil((1-sparsity)·nB)
+                             rounded up to a multiple of budget_multiple,
+                             clamped to [1, nB]; nB when dense              */
     int32_t max_row_len;  /* longest row of the block list                  */
     int64_t nnz_per_head; /* kept (query block, key block) pairs per (b, h) */
     int64_t nnz;          /* B·H·nnz_per_head: length of the col array      */
@@ -123,6 +140,9 @@ typedef struct {
     int32_t dense;        /* 1 when every block is kept (no selection)      */
     int32_t tile[3];      /* resolved tile                                  */
     int32_t rope_split[3];/* resolved RoPE split                            */
+    int32_t scorer;       /* resolved scorer                                */
+    int32_t subblocks;    /* resolved runs per block (1 for the mean scorer) */
+    int32_t budget_multiple; /* resolved budget multiple                    */
 } sva_plan_info;
 
 /* ---- host-only calls (no device needed) ---- */
@@ -174,9 +194,9 @@ int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* s
 
 /* Block selection.  q_r: tile order [B, H, Np, d] (SVA_FORWARD of Q');
  * k_t: K tiles (SVA_FORWARD_KT of K', the same buffer sva_attention reads).
- * For every (b, h, query block qb): score(kb) = mean(Q' rows of qb) ·
- * mean(K' rows of kb), means over valid tokens; keep the forced blocks and
- * then the best-scored blocks (score descending, lower block index first on
+ * For every (b, h, query block qb): score(kb) by the plan's scorer (means
+ * over valid tokens, float64); keep the forced blocks and then the
+ * best-scored blocks (score descending, lower block index first on
  * equal scores) until the row holds row_ptr[qb+1] - row_ptr[qb] blocks.
  * Writes `col` [nnz] int32, each row in ascending block order.  `workspace`
  * (device, info.select_workspace_bytes) holds the block means.  Nothing to

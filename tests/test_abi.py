@@ -29,13 +29,19 @@ def test_library_exports_every_declared_symbol():
 
 def _geom(wl):
     return O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
-                      sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+                      sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra,
+                      split=wl.rope_split, scorer=wl.scorer, subblocks=wl.subblocks,
+                      budget_multiple=max(1, wl.budget_multiple))
 
 
 CASES = list(I.WORKLOADS.values()) + [
     I.custom("ragged", 2, 3, 5, 13, 17, 128, 128, 0.6, flags=I.KEEP_SAME_FRAME,
              n_extra=128),
     I.custom("ragged64", 1, 2, 3, 7, 11, 64, 64, 0.5, tile=(2, 3, 4), n_extra=64),
+    I.custom("subblock8", 1, 2, 5, 16, 24, 128, 64, 0.75, tile=(1, 4, 16),
+             scorer=1, budget_multiple=8),
+    I.custom("subblock8_wide", 1, 1, 21, 45, 80, 128, 128, 0.8, scorer=1, subblocks=2,
+             budget_multiple=8, flags=I.KEEP_SAME_FRAME),
 ]
 
 
@@ -80,11 +86,17 @@ def test_workload_block_lists():
     (dict(rope_split=(64, 64, 64)), S.SVA_ERR_INVALID_ARG),
     (dict(eps=-1.0), S.SVA_ERR_INVALID_ARG),
     (dict(rope_theta=0.5), S.SVA_ERR_INVALID_ARG),
+    (dict(scorer=2), S.SVA_ERR_INVALID_ARG),
+    (dict(scorer=1, subblocks=3), S.SVA_ERR_UNSUPPORTED),
+    (dict(scorer=1, subblocks=8), S.SVA_ERR_UNSUPPORTED),
+    (dict(scorer=0, subblocks=4), S.SVA_ERR_INVALID_ARG),
+    (dict(budget_multiple=-1), S.SVA_ERR_INVALID_ARG),
 ])
 def test_argument_errors(kw, status):
     base = dict(B=1, H=2, T=4, Hh=8, W=8, d=128, block=128, sparsity=0.5)
     extra = {k: kw.pop(k) for k in list(kw) if k in ("tile", "n_extra", "rope_split", "eps",
-                                                     "rope_theta", "flags")}
+                                                     "rope_theta", "flags", "scorer",
+                                                     "subblocks", "budget_multiple")}
     base.update(kw)
     desc = S.sva_plan_desc_init(base["B"], base["H"], base["T"], base["Hh"], base["W"],
                                 base["d"], base["block"], base["sparsity"],

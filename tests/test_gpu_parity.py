@@ -47,6 +47,12 @@ SMALL = {
     "partial96": I.custom("partial96", 1, 2, 4, 8, 24, 128, 128, 0.5,
                           flags=I.KEEP_SAME_FRAME, n_extra=128, seed_base=9700,
                           rope_split=(32, 32, 32)),
+    # SubBlock scorer: 4 runs of 32 tokens, budget rounded up to 8 blocks
+    "sub128": I.custom("sub128", 1, 2, 5, 16, 24, 128, 128, 0.6, seed_base=9800,
+                       scorer=1, budget_multiple=8),
+    # SubBlock scorer, 64-token blocks in 2 runs, ragged tail, extra tokens
+    "sub64": I.custom("sub64", 2, 2, 3, 10, 14, 64, 64, 0.5, tile=(2, 4, 8), n_extra=64,
+                      seed_base=9900, scorer=1, subblocks=2),
 }
 
 
@@ -274,7 +280,7 @@ def test_binding_rejects_bad_tensors():
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["wan480p_dense", "wan480p_sp75", "wan720p_sp75", "hunyuan720p_sp80",
-        "hunyuan720p_dense", "packed768p_sp80"]
+        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock"]
 _full_cache = {}
 
 
@@ -342,8 +348,13 @@ def test_full_workload_sampled(name):
         qr_f = O.bf16_bits_to_f64(qr_g)
         kr_f = O.bf16_bits_to_f64(kr_g)
         if col is not None:
-            kept_ref, scores, thresh, smax = O.select_blocks(
-                O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]), g, meta)
+            if g.scorer == O.SCORER_SUBBLOCK:
+                sc_ref = O.subblock_scores(O.subblock_means(qr_f, g, meta[0]),
+                                           O.subblock_means(kr_f, g, meta[0]), g, meta[0])
+                kept_ref, scores, thresh, smax = O.select_from_scores(sc_ref, g, meta)
+            else:
+                kept_ref, scores, thresh, smax = O.select_blocks(
+                    O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]), g, meta)
             kept_g = kept_from_col(col[h * nnz:(h + 1) * nnz], row_ptr, g.nB)
             n, e = compare_masks(kept_g, kept_ref, scores, thresh, smax, forced)
             stats["mask_diffs"] += n
