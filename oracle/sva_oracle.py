@@ -28,7 +28,9 @@ notes and repeated next to each function):
 5. Exact softmax attention of each query over the valid keys of its kept
    blocks, non-causal (same section: the sparse path serves non-causal DiT
    attention and never builds the full attention matrix).  With every block
-   kept this is textbook dense attention.
+   kept this is textbook dense attention.  Optionally the dropped blocks
+   enter the softmax as their mean key and value weighted by their size
+   (compensation; the Sol-Attn README and the Sol blog's 4.2.2 on PISA).
 6. The inverse permutation of the output.
 
 Rounding: the only roundings modelled are the two bf16 storage points of
@@ -45,6 +47,7 @@ import numpy as np
 
 SVA_DENSE = 1
 SVA_KEEP_SAME_FRAME = 2
+SVA_COMPENSATE = 4
 SCORER_MEAN = 0
 SCORER_SUBBLOCK = 1
 
@@ -460,6 +463,16 @@ def block_attention(qr, kr, vr, kept, geom: Geometry, meta=None, qblocks=None):
     in two passes (max, then exp and sum).  Padding query rows are zero.
     Only the query blocks in ``qblocks`` (default all) are computed; the
     others are left at zero.
+
+    With the compensate flag, every key block dropped from the row also
+    enters the softmax, as its mean key and mean value (over its valid
+    tokens) weighted by its valid count |B|: one extra logit
+    q_p·k̄_B / sqrt(d) + ln|B| with value v̄_B per dropped block.  The pages
+    name a light-weight compensation of the dropped blocks (the Sol-Attn
+    README) and a first-order Taylor compensation (PISA, in the Sol blog's
+    4.2.2); this is the leading term of that expansion: summed over the
+    block, the first-order term of exp(q·k_j) around k̄_B vanishes, and the
+    value term it leaves out would need a d×d moment per block.
     """
     valid, _, _, _ = block_meta(geom) if meta is None else meta
     b, d = geom.block, geom.d
@@ -468,15 +481,26 @@ def block_attention(qr, kr, vr, kept, geom: Geometry, meta=None, qblocks=None):
     v = np.asarray(vr, np.float64)
     out = np.zeros((geom.Np, d), dtype=np.float64)
     scale = 1.0 / math.sqrt(d)
+    comp = bool(geom.flags & SVA_COMPENSATE)
+    if comp:
+        kbar = np.stack([k[kb * b: kb * b + valid[kb]].mean(axis=0) for kb in range(geom.nB)])
+        vbar = np.stack([v[kb * b: kb * b + valid[kb]].mean(axis=0) for kb in range(geom.nB)])
     rows = range(geom.nB) if qblocks is None else qblocks
     for qb in rows:
         keys = np.concatenate([np.arange(kb * b, kb * b + valid[kb])
                                for kb in np.nonzero(kept[qb])[0]])
         qs = q[qb * b: qb * b + valid[qb]]
         logits = (qs @ k[keys].T) * scale
+        vals = v[keys]
+        if comp:
+            drop = np.nonzero(~kept[qb])[0]
+            if drop.size:
+                extra = (qs @ kbar[drop].T) * scale + np.log(valid[drop].astype(np.float64))
+                logits = np.concatenate([logits, extra], axis=1)
+                vals = np.concatenate([vals, vbar[drop]], axis=0)
         m = logits.max(axis=1, keepdims=True)
         e = np.exp(logits - m)
-        out[qb * b: qb * b + valid[qb]] = (e @ v[keys]) / e.sum(axis=1, keepdims=True)
+        out[qb * b: qb * b + valid[qb]] = (e @ vals) / e.sum(axis=1, keepdims=True)
     return out
 
 

@@ -500,6 +500,68 @@ def test_attention_bruteforce_loops():
             assert abs(out[p, c] - want) < 1e-12
 
 
+def check_compensation_exact():
+    """Dropped blocks whose keys and values are constant: the compensated
+    sparse attention is exactly dense attention (brute force)."""
+    g = O.Geometry(B=1, H=1, T=2, Hh=6, W=10, d=32, block=64, sparsity=0.5, tile=(1, 6, 10),
+                   n_extra=64, flags=O.SVA_COMPENSATE)
+    valid, _, _, _ = O.block_meta(g)
+    rng = np.random.default_rng(31)
+    qr = rng.standard_normal((g.Np, g.d))
+    kr = rng.standard_normal((g.Np, g.d))
+    vr = rng.standard_normal((g.Np, g.d))
+    kept = np.ones((g.nB, g.nB), bool)
+    kept[0, 1] = False                  # query block 0 drops block 1 (ragged, 56 valid)
+    kept[1, 0] = False                  # query block 1 drops block 0
+    for kb in (0, 1):                   # make the dropped blocks constant
+        kr[kb * g.block: kb * g.block + valid[kb]] = rng.standard_normal(g.d)
+        vr[kb * g.block: kb * g.block + valid[kb]] = rng.standard_normal(g.d)
+    for x in (qr, kr, vr):              # padding rows are zero, as after the reorder
+        x[g.block + valid[1]: 2 * g.block] = 0.0
+    got = O.block_attention(qr, kr, vr, kept, g)
+    want = O.block_attention(qr, kr, vr, np.ones_like(kept), g)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # and it differs from the uncompensated sparse attention
+    g0 = O.Geometry(B=1, H=1, T=2, Hh=6, W=10, d=32, block=64, sparsity=0.5, tile=(1, 6, 10),
+                    n_extra=64)
+    assert np.abs(O.block_attention(qr, kr, vr, kept, g0) - want).max() > 1e-3
+
+
+def test_compensation_exact_on_constant_dropped_blocks():
+    check_compensation_exact()
+
+
+def test_compensation_brute_force():
+    """Brute force with loops: every dropped block contributes |B| copies of
+    (mean key, mean value) to the softmax of each query row."""
+    g = O.Geometry(B=1, H=1, T=2, Hh=4, W=8, d=16, block=16, sparsity=0.5, tile=(1, 4, 4),
+                   flags=O.SVA_COMPENSATE)
+    valid, _, _, _ = O.block_meta(g)
+    rng = np.random.default_rng(32)
+    qr, kr, vr = (rng.standard_normal((g.Np, g.d)) for _ in range(3))
+    kept = rng.random((g.nB, g.nB)) < 0.5
+    kept[np.arange(g.nB), np.arange(g.nB)] = True
+    got = O.block_attention(qr, kr, vr, kept, g)
+    for qb in range(g.nB):
+        for p in range(qb * g.block, qb * g.block + valid[qb]):
+            num = np.zeros(g.d)
+            den = 0.0
+            for kb in range(g.nB):
+                rows = range(kb * g.block, kb * g.block + valid[kb])
+                if kept[qb, kb]:
+                    for j in rows:
+                        w = math.exp(sum(qr[p, i] * kr[j, i] for i in range(g.d)) / math.sqrt(g.d))
+                        num += w * vr[j]
+                        den += w
+                else:
+                    km = sum(kr[j] for j in rows) / valid[kb]
+                    vm = sum(vr[j] for j in rows) / valid[kb]
+                    w = valid[kb] * math.exp(sum(qr[p, i] * km[i] for i in range(g.d)) / math.sqrt(g.d))
+                    num += w * vm
+                    den += w
+            np.testing.assert_allclose(got[p], num / den, rtol=1e-10, atol=1e-12)
+
+
 def test_attention_row_sums_are_one():
     g, qr, kr, vr, valid = _attn_case(14, sparsity=0.5)
     kept = np.eye(g.nB, dtype=bool) | (np.arange(g.nB)[None, :] == 0)
@@ -617,13 +679,38 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "block_attention", bad_attn2)
     assert _fails(check_sparse_attention_masked_sdpa)
     monkeypatch.setattr(O, "block_attention", orig_attn)
-    # 9. SubBlock estimate without the sub-block counts
+    # 9. compensation without the block-size weight (each dropped block
+    #    counted once instead of |B| times)
+    orig_attn2 = O.block_attention
+    def bad_comp(qr, kr, vr, kept, g, meta=None, qblocks=None):
+        if not (g.flags & O.SVA_COMPENSATE):
+            return orig_attn2(qr, kr, vr, kept, g, meta, qblocks)
+        valid = O.block_meta(g)[0]
+        b, out = g.block, np.zeros((g.Np, g.d))
+        for qb in range(g.nB):
+            keys = np.concatenate([np.arange(kb * b, kb * b + valid[kb])
+                                   for kb in np.nonzero(kept[qb])[0]])
+            qs = np.asarray(qr)[qb * b: qb * b + valid[qb]]
+            lg = qs @ np.asarray(kr)[keys].T / math.sqrt(g.d)
+            vals = np.asarray(vr)[keys]
+            for kb in np.nonzero(~kept[qb])[0]:
+                km = np.asarray(kr)[kb * b: kb * b + valid[kb]].mean(axis=0)
+                vm = np.asarray(vr)[kb * b: kb * b + valid[kb]].mean(axis=0)
+                lg = np.concatenate([lg, (qs @ km)[:, None] / math.sqrt(g.d)], axis=1)
+                vals = np.concatenate([vals, vm[None]], axis=0)
+            e = np.exp(lg - lg.max(axis=1, keepdims=True))
+            out[qb * b: qb * b + valid[qb]] = e @ vals / e.sum(axis=1, keepdims=True)
+        return out
+    monkeypatch.setattr(O, "block_attention", bad_comp)
+    assert _fails(check_compensation_exact)
+    monkeypatch.setattr(O, "block_attention", orig_attn2)
+    # 10. SubBlock estimate without the sub-block counts
     orig_cnt = O.subblock_counts
     monkeypatch.setattr(O, "subblock_counts",
                         lambda g, valid=None: np.minimum(orig_cnt(g, valid), 1))
     assert _fails(check_subblock_exact)
     monkeypatch.setattr(O, "subblock_counts", orig_cnt)
-    # 10. SubBlock estimate with the max instead of the sum over sub-block pairs
+    # 11. SubBlock estimate with the max instead of the sum over sub-block pairs
     orig_sub = O.subblock_scores
     def bad_sub(qs, ks, g, valid=None):
         cnt = O.subblock_counts(g, valid).astype(float)
