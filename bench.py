@@ -90,7 +90,12 @@ def main():
         if not info.dense:
             S.sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col)
         rec(4)
-        S.sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r)
+        if plan.compensated:
+            S.sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t)
+            S.sva_attention_compensated(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t,
+                                        buf.vm_t, buf.o_r)
+        else:
+            S.sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r)
         rec(5)
         S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
         rec(6)

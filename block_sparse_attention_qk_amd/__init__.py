@@ -27,6 +27,7 @@ SVA_ERR_HIP = -4
 
 SVA_DENSE = 1
 SVA_KEEP_SAME_FRAME = 2
+SVA_COMPENSATE = 4
 
 SVA_SCORER_MEAN = 0
 SVA_SCORER_SUBBLOCK = 1
@@ -40,6 +41,7 @@ EXPORTED = (
     "sva_plan_desc_init", "sva_plan_query", "sva_plan_host_tables",
     "sva_plan_create", "sva_plan_create_ex", "sva_plan_get_info", "sva_destroy",
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
+    "sva_block_means", "sva_attention_compensated",
     "sva_status_string", "sva_last_error",
 )
 
@@ -72,7 +74,7 @@ class sva_plan_info(ctypes.Structure):
         ("tile", ctypes.c_int32 * 3),
         ("rope_split", ctypes.c_int32 * 3),
         ("scorer", ctypes.c_int32), ("subblocks", ctypes.c_int32),
-        ("budget_multiple", ctypes.c_int32),
+        ("budget_multiple", ctypes.c_int32), ("n_mean_groups", ctypes.c_int32),
     ]
 
 
@@ -101,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.sva_reorder.argtypes = [vp, vp, vp, i, vp]
     L.sva_select_blocks.argtypes = [vp, vp, vp, vp, sz, vp, vp]
     L.sva_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.sva_block_means.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.sva_attention_compensated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
     L.sva_last_error.argtypes = []
@@ -235,6 +239,20 @@ class Plan:
         d = self.desc
         return (d.B, d.H, int(self.info.nB), d.block // 32, d.d // 16, 64, 8)
 
+    @property
+    def km_shape(self):
+        d = self.desc
+        return (d.B, d.H, int(self.info.n_mean_groups), d.d // 16, 64, 8)
+
+    @property
+    def vm_shape(self):
+        d = self.desc
+        return (d.B, d.H, int(self.info.n_mean_groups), 4, d.d, 8)
+
+    @property
+    def compensated(self) -> bool:
+        return bool(self.desc.flags & SVA_COMPENSATE) and not self.info.dense
+
     def host_tables(self, forced=False):
         return sva_plan_host_tables(self.desc, forced)
 
@@ -321,6 +339,31 @@ def sva_attention(plan: Plan, q_r, k_t, v_t, col, o_r, stream=None) -> None:
                                _tensor(o_r, ts, torch.bfloat16, "o_r"), _stream(stream)))
 
 
+def sva_block_means(plan: Plan, k_t, v_t, km_t, vm_t, stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    _check(lib().sva_block_means(plan.handle, _tensor(k_t, plan.kt_shape, bf, "k_t"),
+                                 _tensor(v_t, plan.vt_shape, bf, "v_t"),
+                                 _tensor(km_t, plan.km_shape, bf, "km_t"),
+                                 _tensor(vm_t, plan.vm_shape, bf, "vm_t"), _stream(stream)))
+
+
+def sva_attention_compensated(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o_r,
+                              stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    ts = plan.tile_shape
+    c = None
+    if col is not None:
+        c = _tensor(col, (int(plan.info.nnz),), torch.int32, "col")
+    elif not plan.info.dense:
+        raise ValueError("col is required for a sparse plan")
+    _check(lib().sva_attention_compensated(
+        plan.handle, _tensor(q_r, ts, bf, "q_r"), _tensor(k_t, plan.kt_shape, bf, "k_t"),
+        _tensor(v_t, plan.vt_shape, bf, "v_t"), c, _tensor(km_t, plan.km_shape, bf, "km_t"),
+        _tensor(vm_t, plan.vm_shape, bf, "vm_t"), _tensor(o_r, ts, bf, "o_r"), _stream(stream)))
+
+
 def sva_status_string(status: int) -> str:
     return lib().sva_status_string(status).decode()
 
@@ -348,6 +391,11 @@ class Buffers:
         self.o = torch.empty(plan.raster_shape, dtype=bf, device=device)
         nnz = int(plan.info.nnz) if not plan.info.dense else 0
         self.col = torch.empty(nnz, dtype=torch.int32, device=device) if nnz else None
+        if plan.compensated:
+            self.km_t = torch.empty(plan.km_shape, dtype=bf, device=device)
+            self.vm_t = torch.empty(plan.vm_shape, dtype=bf, device=device)
+        else:
+            self.km_t = self.vm_t = None
         ws = int(plan.info.select_workspace_bytes)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
 
@@ -361,6 +409,11 @@ def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
     sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
     if not plan.info.dense:
         sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
-    sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r, stream)
+    if plan.compensated:
+        sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
+        sva_attention_compensated(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
+                                  buf.o_r, stream)
+    else:
+        sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r, stream)
     sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
     return buf.o

@@ -60,6 +60,8 @@ struct AttnArgs {
     const u32x4_t* k;    // K tiles [B,H,nB,BLK/32,d/16,64,8]
     const u32x4_t* vt;   // V tiles [B,H,nB,BLK/32,4,d,8]
     const int32_t* col;  // [B,H,nnz_per_head]
+    const u32x4_t* km;   // block-mean K tiles [B,H,n_mean_groups,d/16,64,8], or NULL
+    const u32x4_t* vm;   // block-mean V tiles [B,H,n_mean_groups,4,d,8]
     uint2* o;            // [B,H,Np,d]
 };
 
@@ -130,7 +132,7 @@ constexpr int attn_stage_buffers(int d, int blk) {
 // waves per SIMD the register budget is sized for (LDS decides the rest)
 constexpr int attn_min_waves(int d, int blk) { return (d == 128 && blk == 64) ? 1 : 2; }
 
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool COMP>
 __global__ __launch_bounds__(BLK * 2)
 __attribute__((amdgpu_waves_per_eu(attn_min_waves(D, BLK), 2)))
 void attn_kernel(AttnArgs a) {
@@ -153,7 +155,8 @@ void attn_kernel(AttnArgs a) {
     constexpr int kWaitNext = (kInFlight & 15) | ((kInFlight >> 4) << 14) | (0x7 << 4) | (0xF << 8);
     __shared__ u32x4_t sK[NBUF][CPS];
     __shared__ u32x4_t sV[NBUF][CPS];
-    extern __shared__ int32_t s_col[];   // this row's block list (sparse plans)
+    extern __shared__ int32_t s_col[];   // this row's block list (sparse plans),
+                                         // then a bitmap of it (compensation)
 
     const DevPlan& p = a.p;
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -254,7 +257,7 @@ void attn_kernel(AttnArgs a) {
     ([&](int sl_) {                                                                  \
         const int kb_ = SVA_KB(sl_);                                                 \
         return (sl_ >= nstage || kb_ < 0) ? 0                                        \
-             : (kb_ == last_video ? last_valid - (sl_ % SPB) * SK : SK);             \
+             : (kb_ == last_video ? min(last_valid - (sl_ % SPB) * SK, SK) : SK);    \
     }(st))
     // row max of SC over every key
 #define SVA_MAX(SC, MX)                                                              \
@@ -372,6 +375,73 @@ void attn_kernel(AttnArgs a) {
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // no copy left in flight at exit
+
+    // Compensation (sparse rows that drop blocks): every block the row does
+    // not list enters the softmax as one extra key, its mean key with logit
+    // bias log2|B| and its mean value (the mean tiles hold block kb as key
+    // kb % 32 of group kb / 32).  One stage per group of 32 means, after the
+    // kept stages, two buffer pairs alternating.
+    if constexpr (COMP) {
+        const int ng = p.n_mean_groups;
+        if (len < p.nB) {
+            uint32_t* s_kept = reinterpret_cast<uint32_t*>(s_col + p.max_row_len);
+            for (int i = tid; i < ng; i += NT) s_kept[i] = 0u;
+            // every wave's copies have landed and every read of the stage
+            // buffers is done before they are reused
+            __syncthreads();
+            for (int i = tid; i < len; i += NT) {
+                const int kb = s_col[i];
+                if (kb >= 0 && kb < p.nB) atomicOr(&s_kept[kb >> 5], 1u << (kb & 31));
+            }
+            const u32x4_t* kmb = a.km + bh * (int64_t)ng * CPS + lane;
+            const u32x4_t* vmb = a.vm + bh * (int64_t)ng * CPS + lane;
+            const float bias_blk = __log2f((float)BLK) / c;
+            const float bias_last = __log2f((float)last_valid) / c;
+            auto copy = [&](int cg, u32x4_t* KB, u32x4_t* VB) {
+#pragma unroll
+                for (int i = 0; i < LPW; ++i) {
+                    const int e = (i * NWV + wave_u) * 64;
+                    lds_dma16(kmb + (int64_t)cg * CPS + e, lds_addr(KB + e));
+                    lds_dma16(vmb + (int64_t)cg * CPS + e, lds_addr(VB + e));
+                }
+            };
+            auto stage = [&](int cg, const u32x4_t* KB, const u32x4_t* VB) {
+                f32x16_t sm;
+                SVA_SCORE(KB, sm);
+                const uint32_t kept = s_kept[cg];
+                float mm = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    // lane (j, hf) holds stage keys 8*(v/4) + 4*hf + v%4
+                    const int key = 8 * (v / 4) + 4 * hf + (v % 4);
+                    const int kb = cg * 32 + key;
+                    const bool in = kb < p.nB && !((kept >> key) & 1u);
+                    sm[v] = in ? sm[v] + (kb == last_video ? bias_last : bias_blk) : -INFINITY;
+                    mm = fmaxf(mm, sm[v]);
+                }
+                mm = lane_swap_max(mm) * c;
+                SVA_RESCALE(mm);
+                bf16x8_t pm[2];
+                SVA_EXP(sm, pm);
+                SVA_PV(VB, pm);
+            };
+            copy(0, sK[0], sV[0]);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();          // copies of group 0 and the bitmap visible
+            for (int cg = 0; cg < ng; cg += 2) {
+                if (cg + 1 < ng) copy(cg + 1, sK[1], sV[1]);
+                stage(cg, sK[0], sV[0]);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __builtin_amdgcn_s_barrier();
+                if (cg + 1 < ng) {
+                    if (cg + 2 < ng) copy(cg + 2, sK[0], sV[0]);
+                    stage(cg + 1, sK[1], sV[1]);
+                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+        }
+    }
 #undef SVA_PV
 #undef SVA_EXP
 #undef SVA_RESCALE
@@ -402,28 +472,39 @@ void attn_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
-                            const uint16_t* vt, const int32_t* col, uint16_t* o, hipStream_t s) {
+                            const uint16_t* vt, const int32_t* col, const uint16_t* km,
+                            const uint16_t* vm, uint16_t* o, hipStream_t s) {
     AttnArgs a;
     a.p = p;
     a.q = reinterpret_cast<const u32x4_t*>(qr);
     a.k = reinterpret_cast<const u32x4_t*>(kr);
     a.vt = reinterpret_cast<const u32x4_t*>(vt);
     a.col = col;
+    a.km = reinterpret_cast<const u32x4_t*>(km);
+    a.vm = reinterpret_cast<const u32x4_t*>(vm);
     a.o = reinterpret_cast<uint2*>(o);
     dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
     dim3 block(p.block * 2);
-    const size_t lds = p.dense ? 0 : (size_t)p.max_row_len * sizeof(int32_t);
+    const size_t lds = p.dense ? 0
+                     : (size_t)(p.max_row_len + (km ? p.n_mean_groups : 0)) * sizeof(int32_t);
     auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a); };
+    // dense plans have nothing to compensate; compensation is its own
+    // instantiation so the plain kernels carry none of it
     if (p.dense) {
-        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, true>);
-        else if (p.d == 128) launch(attn_kernel<128, 64, true>);
-        else if (p.block == 128) launch(attn_kernel<64, 128, true>);
-        else launch(attn_kernel<64, 64, true>);
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, true, false>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, true, false>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, true, false>);
+        else launch(attn_kernel<64, 64, true, false>);
+    } else if (!km) {
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, false>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, false, false>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, false, false>);
+        else launch(attn_kernel<64, 64, false, false>);
     } else {
-        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false>);
-        else if (p.d == 128) launch(attn_kernel<128, 64, false>);
-        else if (p.block == 128) launch(attn_kernel<64, 128, false>);
-        else launch(attn_kernel<64, 64, false>);
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, true>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, false, true>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, false, true>);
+        else launch(attn_kernel<64, 64, false, true>);
     }
     return hipGetLastError();
 }

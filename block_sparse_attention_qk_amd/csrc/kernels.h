@@ -37,6 +37,7 @@ struct DevPlan {
     int same_frame;     // SVA_KEEP_SAME_FRAME
     int scorer;         // SVA_SCORER_*
     int nsub;           // runs per block (1 for the mean scorer)
+    int n_mean_groups;  // ceil(nB / 32)
     float eps;
     int rope_off[3];    // offsets (in cos/sin pairs) of the t, h, w tables
     int rope_half[3];   // rotated pairs per section
@@ -65,8 +66,13 @@ hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, i
 hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s);
 
+// km, vm: mean tiles (NULL: no compensation)
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
-                            const uint16_t* vt, const int32_t* col, uint16_t* o, hipStream_t s);
+                            const uint16_t* vt, const int32_t* col, const uint16_t* km,
+                            const uint16_t* vm, uint16_t* o, hipStream_t s);
+
+hipError_t launch_block_means(const DevPlan& p, const uint16_t* kt, const uint16_t* vt,
+                              uint16_t* km, uint16_t* vm, hipStream_t s);
 
 // ---- small device helpers shared by the kernels ----
 

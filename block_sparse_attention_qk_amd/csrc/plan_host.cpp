@@ -40,7 +40,7 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
         return fail(err, SVA_ERR_UNSUPPORTED, "block must be 64 or 128");
     if (!(d.sparsity >= 0.0 && d.sparsity < 1.0))
         return fail(err, SVA_ERR_INVALID_ARG, "sparsity must be in [0, 1)");
-    if (d.flags & ~(SVA_DENSE | SVA_KEEP_SAME_FRAME))
+    if (d.flags & ~(SVA_DENSE | SVA_KEEP_SAME_FRAME | SVA_COMPENSATE))
         return fail(err, SVA_ERR_INVALID_ARG, "unknown flag bits");
     if (d.tile_t == 0 && d.tile_h == 0 && d.tile_w == 0) {
         if (d.block == 64) { d.tile_t = 4; d.tile_h = 4; d.tile_w = 4; }
@@ -114,6 +114,7 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     I.scorer = d.scorer;
     I.subblocks = d.subblocks;
     I.budget_multiple = d.budget_multiple;
+    I.n_mean_groups = (int32_t)((nB + 31) / 32);
     for (int a = 0; a < 3; ++a) I.rope_split[a] = d.rope_split[a];
 
     // --- permutation ---

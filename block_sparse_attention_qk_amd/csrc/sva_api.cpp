@@ -149,6 +149,7 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.same_frame = (ds.flags & SVA_KEEP_SAME_FRAME) ? 1 : 0;
     d.scorer = I.scorer;
     d.nsub = I.subblocks;
+    d.n_mean_groups = I.n_mean_groups;
     d.eps = (float)ds.eps;
     for (int a = 0; a < 3; ++a) {
         d.rope_off[a] = h.rope_off[a];
@@ -250,7 +251,48 @@ int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
     hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
                                          static_cast<const uint16_t*>(k_t),
+                                         static_cast<const uint16_t*>(v_t), col, nullptr,
+                                         nullptr, static_cast<uint16_t*>(o_r),
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "attention launch");
+    return SVA_OK;
+}
+
+int sva_block_means(sva_plan plan, const void* k_t, const void* v_t, void* km_t, void* vm_t,
+                    void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!k_t || !v_t || !km_t || !vm_t)
+        return set_err(SVA_ERR_INVALID_ARG, "k_t, v_t, km_t and vm_t must be non-NULL");
+    if (!sva::aligned16(k_t) || !sva::aligned16(v_t) || !sva::aligned16(km_t) ||
+        !sva::aligned16(vm_t))
+        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    hipError_t e = sva::launch_block_means(plan->dev, static_cast<const uint16_t*>(k_t),
+                                           static_cast<const uint16_t*>(v_t),
+                                           static_cast<uint16_t*>(km_t),
+                                           static_cast<uint16_t*>(vm_t),
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "block means launch");
+    return SVA_OK;
+}
+
+int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
+                              const void* v_t, const int32_t* col, const void* km_t,
+                              const void* vm_t, void* o_r, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!q_r || !k_t || !v_t || !o_r || !km_t || !vm_t)
+        return set_err(SVA_ERR_INVALID_ARG,
+                       "q_r, k_t, v_t, km_t, vm_t and o_r must be non-NULL");
+    if (!plan->host.info.dense && !col)
+        return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
+    if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(v_t) ||
+        !sva::aligned16(o_r) || !sva::aligned16(km_t) || !sva::aligned16(vm_t) ||
+        ((uintptr_t)col & 3u))
+        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
+                                         static_cast<const uint16_t*>(k_t),
                                          static_cast<const uint16_t*>(v_t), col,
+                                         static_cast<const uint16_t*>(km_t),
+                                         static_cast<const uint16_t*>(vm_t),
                                          static_cast<uint16_t*>(o_r),
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "attention launch");

@@ -25,6 +25,7 @@ import numpy as np
 
 DENSE = 1
 KEEP_SAME_FRAME = 2
+COMPENSATE = 4
 
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
 _STREAM_TAU = 3
@@ -84,6 +85,9 @@ WORKLOADS = {
     # packed video + 512 audio/text tokens (always-dense rows and columns)
     "packed768p_sp80": Workload("packed768p_sp80", 1, 48, 31, 48, 84, 128, 128, 0.80,
                                 tile=(2, 8, 8), n_extra=512, seed_base=4000),
+    # HunyuanVideo-like inputs with the dropped blocks compensated
+    "hunyuan720p_comp": Workload("hunyuan720p_comp", 1, 24, 33, 45, 80, 128, 128, 0.80,
+                                 flags=COMPENSATE, tile=(2, 8, 8), seed_base=3000),
     # the 720p inputs under the SubBlock scorer (4 runs of 32 tokens per
     # block, budget rounded up to a multiple of 8 blocks)
     "wan720p_subblock": Workload("wan720p_subblock", 1, 40, 21, 45, 80, 128, 128, 0.75,

@@ -76,6 +76,9 @@ extern "C" {
                                    the dense warm-up steps of the pages */
 #define SVA_KEEP_SAME_FRAME  2u /* always keep key blocks whose frame range
                                    meets the query block's frame range */
+#define SVA_COMPENSATE       4u /* the step uses sva_attention_compensated:
+                                   dropped key blocks enter the softmax as
+                                   their mean key and value, weighted by size */
 
 /* ---- block scorers (sva_plan_desc.scorer) ---- */
 #define SVA_SCORER_MEAN      0  /* score = mean(Q' of qb) · mean(K' of kb)     */
@@ -143,6 +146,8 @@ typedef struct {
     int32_t scorer;       /* resolved scorer                                */
     int32_t subblocks;    /* resolved runs per block (1 for the mean scorer) */
     int32_t budget_multiple; /* resolved budget multiple                    */
+    int32_t n_mean_groups;/* ceil(nB / 32): groups of 32 block means in the
+                             mean tiles of sva_block_means                  */
 } sva_plan_info;
 
 /* ---- host-only calls (no device needed) ---- */
@@ -214,6 +219,29 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t,
  * o_r: [B, H, Np, d], padding rows written as zero. */
 int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                   const int32_t* col, void* o_r, void* stream);
+
+/* Block means for compensation.  From the K tiles and V tiles of a step,
+ * the mean key and mean value of every key block over its valid tokens
+ * (float32 sums, rounded to bf16), written as mean tiles in the layouts of
+ * the K and V tiles with block kb as "key" kb % 32 of group kb / 32:
+ *   km_t [B, H, n_mean_groups, d/16, 64, 8]    (K-tile layout)
+ *   vm_t [B, H, n_mean_groups, 4, d, 8]        (V-tile layout)
+ * Entries past nB are zero.  Caller-owned device buffers. */
+int sva_block_means(sva_plan plan, const void* k_t, const void* v_t, void* km_t, void* vm_t,
+                    void* stream);
+
+/* Attention with compensation for the dropped blocks.  As sva_attention,
+ * and every key block that row qb of `col` does not list enters the
+ * softmax of each query of qb as one extra key: logit
+ * q·kbar_B / sqrt(d) + ln|B| (|B| = the block's valid tokens) with value
+ * vbar_B, from the mean tiles of sva_block_means.  The pages name a
+ * light-weight compensation of the dropped blocks (Sol-Attn, "Sol Video
+ * Inference Engine" README) and a first-order Taylor compensation (PISA,
+ * "Sol Video Inference Engine" blog, 4.2.2); this is the leading term of
+ * that expansion.  Dense rows have nothing to compensate. */
+int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
+                              const void* v_t, const int32_t* col, const void* km_t,
+                              const void* vm_t, void* o_r, void* stream);
 
 /* ---- errors ---- */
 const char* sva_status_string(int status);

@@ -53,6 +53,12 @@ SMALL = {
     # SubBlock scorer, 64-token blocks in 2 runs, ragged tail, extra tokens
     "sub64": I.custom("sub64", 2, 2, 3, 10, 14, 64, 64, 0.5, tile=(2, 4, 8), n_extra=64,
                       seed_base=9900, scorer=1, subblocks=2),
+    # compensation of the dropped blocks: ragged 128-token blocks with extra
+    # tokens and same-frame forcing; 64-token blocks, B = 2
+    "comp128": I.custom("comp128", 1, 2, 5, 13, 17, 128, 128, 0.6,
+                        flags=I.COMPENSATE | I.KEEP_SAME_FRAME, n_extra=128, seed_base=10100),
+    "comp64": I.custom("comp64", 2, 2, 3, 10, 14, 64, 64, 0.7, tile=(2, 4, 8),
+                       flags=I.COMPENSATE, seed_base=10200),
 }
 
 
@@ -207,7 +213,12 @@ def test_attention_parity(name):
         vt[b, h] = _vt_from_vr(O.f64_to_bf16_bits(r["vr"]), g)
         kept[b, h] = r["kept"]
     col = None if run.plan.info.dense else dev_col(_col_from_kept(kept, g, B, H))
-    S.sva_attention(run.plan, dev(qr), dev(kt), dev(vt), col, run.buf.o_r)
+    if run.plan.compensated:
+        S.sva_block_means(run.plan, dev(kt), dev(vt), run.buf.km_t, run.buf.vm_t)
+        S.sva_attention_compensated(run.plan, dev(qr), dev(kt), dev(vt), col, run.buf.km_t,
+                                    run.buf.vm_t, run.buf.o_r)
+    else:
+        S.sva_attention(run.plan, dev(qr), dev(kt), dev(vt), col, run.buf.o_r)
     torch.cuda.synchronize()
     out = host_f64(run.buf.o_r)
     worst_rel, worst_abs = 0.0, 0.0
@@ -224,6 +235,41 @@ def test_attention_parity(name):
 
 def dev_col(col_np):
     return torch.from_numpy(col_np).cuda()
+
+
+@pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].flags & I.COMPENSATE])
+def test_block_means_parity(name):
+    """Mean tiles: every block's mean key and value within one bf16 step of
+    the oracle's float64 means (float32 sums on the GPU), zero past nB."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    B, H = wl.B, wl.H
+    kt = np.zeros((B, H, g.nB, g.block // 32, g.d // 16, 64, 8), np.uint16)
+    vt = np.zeros((B, H, g.nB, g.block // 32, 4, g.d, 8), np.uint16)
+    for (b, h), r in ref.items():
+        kt[b, h] = _kt_from_kr(O.f64_to_bf16_bits(r["kr"]), g)
+        vt[b, h] = _vt_from_vr(O.f64_to_bf16_bits(r["vr"]), g)
+    S.sva_block_means(run.plan, dev(kt), dev(vt), run.buf.km_t, run.buf.vm_t)
+    torch.cuda.synchronize()
+    km = host_f64(run.buf.km_t)
+    vm = host_f64(run.buf.vm_t)
+    nG = int(run.plan.info.n_mean_groups)
+    slots = np.arange(nG * 32)
+    for (b, h), r in ref.items():
+        valid = meta[0]
+        # slot layouts: K entry (g, s, hf·32 + j) holds channels 16s + 8hf ..;
+        # V chunk kc = 2(j // 16) + (j % 8 >= 4), slot i = j % 4 + 4 (j % 16 >= 8)
+        kmh = km[b, h].reshape(nG, g.d // 16, 2, 32, 8).transpose(0, 3, 1, 2, 4).reshape(nG * 32, g.d)
+        j = slots % 32
+        kc = 2 * (j // 16) + ((j % 8) >= 4)
+        si = (j % 4) + 4 * ((j % 16) >= 8)
+        vmh = vm[b, h][slots // 32, kc, :, si]
+        for x_got, x in ((kmh, r["kr"]), (vmh, r["vr"])):
+            want = np.stack([x[kb * g.block: kb * g.block + valid[kb]].mean(axis=0)
+                             for kb in range(g.nB)])
+            step = np.abs(O.to_bf16(want * (1 + 2.0 ** -8)) - O.to_bf16(want)) + 2.0 ** -133
+            assert np.all(np.abs(x_got[: g.nB] - want) <= step + np.abs(want) * 2.0 ** -8)
+            assert np.all(x_got[g.nB:] == 0)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -280,7 +326,7 @@ def test_binding_rejects_bad_tensors():
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["wan480p_dense", "wan480p_sp75", "wan720p_sp75", "hunyuan720p_sp80",
-        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock"]
+        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock", "hunyuan720p_comp"]
 _full_cache = {}
 
 
