@@ -1,7 +1,9 @@
 """Benchmark of the whole sparse self-attention step on one MI355X.
 
-One step = QK-RMSNorm + 3D-RoPE, reorder of Q', K' and V, block selection,
-block-sparse attention and the inverse reorder of O, on synthetic inputs
+One step = QK-RMSNorm + 3D-RoPE written straight into the attention layouts,
+reorder of V into V tiles, block selection, block-sparse attention writing O
+straight into raster order (``--staged``: the same with separate reorders
+of Q', K' and O), on synthetic inputs
 already resident in HBM.  Default workload: Wan2.1-14B-like 720p latent
 grid 21×45×80 = 75,600 tokens, 40 heads, d 128, 128-token blocks,
 sparsity 0.75, same-frame key blocks always kept.
@@ -41,6 +43,9 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel that scales the profiler's byte counters)")
+    ap.add_argument("--staged", action="store_true",
+                    help="one call per stage (raster prologue, separate reorders, tile-order "
+                         "attention, inverse reorder) instead of the fused step")
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="heads the CPU oracle runs the whole step on (bounded sample)")
     return ap.parse_args()
@@ -76,29 +81,52 @@ def main():
     buf = S.Buffers(plan)
     stream = torch.cuda.current_stream()
 
+    if args.staged:
+        names = ["prologue", "reorder_qk", "reorder_v", "select", "means", "attention", "reorder_o"]
+    else:
+        names = ["prologue", "reorder_v", "select", "means", "attention"]
+
     def step(ev=None):
-        # ev: 8 events bracketing the stages of this step
-        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
-        rec(0)
-        S.sva_qk_norm_rope(plan, dq, dk, dwq, dwk, buf.qn, buf.kn)
-        rec(1)
-        S.sva_reorder(plan, buf.qn, buf.q_r, S.SVA_FORWARD)
-        S.sva_reorder(plan, buf.kn, buf.k_t, S.SVA_FORWARD_KT)
-        rec(2)
+        # ev: len(names) + 1 events bracketing the stages of this step
+        k = [0]
+
+        def rec():
+            if ev:
+                ev[k[0]].record(stream)
+            k[0] += 1
+
+        rec()
+        if args.staged:
+            # one call per stage: raster prologue, reorders, tile-order
+            # attention, inverse reorder
+            S.sva_qk_norm_rope(plan, dq, dk, dwq, dwk, buf.qn, buf.kn)
+            rec()
+            S.sva_reorder(plan, buf.qn, buf.q_r, S.SVA_FORWARD)
+            S.sva_reorder(plan, buf.kn, buf.k_t, S.SVA_FORWARD_KT)
+            rec()
+        else:
+            # fused: the prologue writes Q' in tile order and K' as K tiles
+            S.sva_qk_norm_rope_tiled(plan, dq, dk, dwq, dwk, buf.q_r, buf.k_t)
+            rec()
         S.sva_reorder(plan, dv, buf.v_t, S.SVA_FORWARD_VT)
-        rec(3)
+        rec()
         if not info.dense:
             S.sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col)
-        rec(4)
+        rec()
         if plan.compensated:
             S.sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t)
-            S.sva_attention_compensated(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t,
-                                        buf.vm_t, buf.o_r)
+        rec()
+        if args.staged:
+            S.sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
+                               buf.o_r, S.SVA_LAYOUT_TILE)
+            rec()
+            S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
+            rec()
         else:
-            S.sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r)
-        rec(5)
-        S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
-        rec(6)
+            # O straight into raster order
+            S.sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
+                               buf.o, S.SVA_LAYOUT_RASTER)
+            rec()
 
     for _ in range(args.warmup):
         step()
@@ -113,7 +141,8 @@ def main():
         del src, dst
 
     # timed region: exactly `steps` steps, per-stage HIP events on the stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -127,7 +156,6 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
 
-    names = ["prologue", "reorder_qk", "reorder_v", "select", "attention", "reorder_o"]
     stage = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events]))
              for i, n in enumerate(names)}
 
@@ -142,10 +170,11 @@ def main():
     sel_bytes = 2.0 * B * H * Np * d * 2 + 2.0 * B * H * nB * d * 8 + 4.0 * nnz
     stage_gbs = {
         "prologue": pro_bytes / (stage["prologue"] * 1e-3) / 1e9,
-        "reorder_qk": 2 * (B * H * (N + Np) * d * 2) / (stage["reorder_qk"] * 1e-3) / 1e9,
         "reorder_v": (B * H * (N + Np) * d * 2) / (stage["reorder_v"] * 1e-3) / 1e9,
-        "reorder_o": (B * H * (N + Np) * d * 2) / (stage["reorder_o"] * 1e-3) / 1e9,
     }
+    if args.staged:
+        stage_gbs["reorder_qk"] = 2 * (B * H * (N + Np) * d * 2) / (stage["reorder_qk"] * 1e-3) / 1e9
+        stage_gbs["reorder_o"] = (B * H * (N + Np) * d * 2) / (stage["reorder_o"] * 1e-3) / 1e9
     if not info.dense:
         stage_gbs["select"] = sel_bytes / (stage["select"] * 1e-3) / 1e9
 
@@ -167,6 +196,7 @@ def main():
             "grid": f"{wl.T}x{wl.Hh}x{wl.W}", "tokens": N, "n_extra": wl.n_extra,
             "block": b, "sparsity": wl.sparsity, "keep_same_frame": bool(wl.flags & I.KEEP_SAME_FRAME),
             "dense": bool(info.dense), "kept_block_pairs": nnz,
+            "path": "staged" if args.staged else "fused",
             "executed_attn_tflop": round(attn_flop / 1e12, 3),
         },
         "roofline": {
@@ -203,9 +233,10 @@ def measured_traffic(workload, d, b):
     src = "k_attention.hip"
     if res.get("sources_sha256", {}).get(src) != PT.source_hashes().get(src):
         return None
-    name = f"attn_kernel<{d}, {b}, false>"
-    e = res.get("kernels", {}).get(name) or res.get("kernels", {}).get(f"attn_kernel<{d}, {b}, true>")
-    return None if e is None else round(e["traffic_bytes"], 0)
+    for name, e in res.get("kernels", {}).items():
+        if name.startswith(f"attn_kernel<{d}, {b}, "):
+            return round(e["traffic_bytes"], 0)
+    return None
 
 
 def cpu_baseline(wl, q, k, v, wq, wk, info, heads, gpu_ms):

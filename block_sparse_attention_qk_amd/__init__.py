@@ -29,6 +29,9 @@ SVA_DENSE = 1
 SVA_KEEP_SAME_FRAME = 2
 SVA_COMPENSATE = 4
 
+SVA_LAYOUT_TILE = 0
+SVA_LAYOUT_RASTER = 1
+
 SVA_SCORER_MEAN = 0
 SVA_SCORER_SUBBLOCK = 1
 
@@ -41,7 +44,8 @@ EXPORTED = (
     "sva_plan_desc_init", "sva_plan_query", "sva_plan_host_tables",
     "sva_plan_create", "sva_plan_create_ex", "sva_plan_get_info", "sva_destroy",
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
-    "sva_block_means", "sva_attention_compensated",
+    "sva_block_means", "sva_attention_compensated", "sva_qk_norm_rope_tiled",
+    "sva_attention_ex",
     "sva_status_string", "sva_last_error",
 )
 
@@ -105,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.sva_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.sva_block_means.argtypes = [vp, vp, vp, vp, vp, vp]
     L.sva_attention_compensated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sva_qk_norm_rope_tiled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sva_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
     L.sva_last_error.argtypes = []
@@ -294,6 +300,20 @@ def sva_qk_norm_rope(plan: Plan, q, k, wq, wk, q_out, k_out, stream=None) -> Non
     _check(lib().sva_qk_norm_rope(plan.handle, *args, _stream(stream)))
 
 
+def sva_qk_norm_rope_tiled(plan: Plan, q, k, wq, wk, q_r, k_t, stream=None) -> None:
+    import torch
+    shp = plan.raster_shape
+    wshape = (plan.desc.H, plan.desc.d)
+    args = [
+        _tensor(q, shp, torch.bfloat16, "q"), _tensor(k, shp, torch.bfloat16, "k"),
+        _tensor(wq, wshape, torch.float32, "wq") if wq is not None else None,
+        _tensor(wk, wshape, torch.float32, "wk") if wk is not None else None,
+        _tensor(q_r, plan.tile_shape, torch.bfloat16, "q_r"),
+        _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
+    ]
+    _check(lib().sva_qk_norm_rope_tiled(plan.handle, *args, _stream(stream)))
+
+
 def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
     import torch
     if direction == SVA_FORWARD:
@@ -364,6 +384,26 @@ def sva_attention_compensated(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o_r,
         _tensor(vm_t, plan.vm_shape, bf, "vm_t"), _tensor(o_r, ts, bf, "o_r"), _stream(stream)))
 
 
+def sva_attention_ex(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout,
+                     stream=None) -> None:
+    import torch
+    bf = torch.bfloat16
+    c = None
+    if col is not None:
+        c = _tensor(col, (int(plan.info.nnz),), torch.int32, "col")
+    elif not plan.info.dense:
+        raise ValueError("col is required for a sparse plan")
+    if (km_t is None) != (vm_t is None):
+        raise ValueError("km_t and vm_t go together")
+    oshape = plan.raster_shape if o_layout == SVA_LAYOUT_RASTER else plan.tile_shape
+    _check(lib().sva_attention_ex(
+        plan.handle, _tensor(q_r, plan.tile_shape, bf, "q_r"),
+        _tensor(k_t, plan.kt_shape, bf, "k_t"), _tensor(v_t, plan.vt_shape, bf, "v_t"), c,
+        _tensor(km_t, plan.km_shape, bf, "km_t") if km_t is not None else None,
+        _tensor(vm_t, plan.vm_shape, bf, "vm_t") if vm_t is not None else None,
+        _tensor(o, oshape, bf, "o"), int(o_layout), _stream(stream)))
+
+
 def sva_status_string(status: int) -> str:
     return lib().sva_status_string(status).decode()
 
@@ -401,8 +441,24 @@ class Buffers:
 
 
 def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
-    """The whole step: prologue, reorders, selection, attention, inverse
-    reorder.  Returns the raster output tensor ``buf.o``."""
+    """The whole step, fused where the library allows: the prologue writes Q'
+    in tile order and K' as K tiles, V is reordered into V tiles, blocks are
+    selected, and the attention writes O straight into raster order.
+    Returns the raster output tensor ``buf.o``."""
+    sva_qk_norm_rope_tiled(plan, q, k, wq, wk, buf.q_r, buf.k_t, stream)
+    sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
+    if not plan.info.dense:
+        sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
+    if plan.compensated:
+        sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
+    sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o,
+                     SVA_LAYOUT_RASTER, stream)
+    return buf.o
+
+
+def forward_staged(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
+    """The same step one call per stage (raster prologue, reorders, tile-order
+    attention, inverse reorder), keeping every intermediate in ``buf``."""
     sva_qk_norm_rope(plan, q, k, wq, wk, buf.qn, buf.kn, stream)
     sva_reorder(plan, buf.qn, buf.q_r, SVA_FORWARD, stream)
     sva_reorder(plan, buf.kn, buf.k_t, SVA_FORWARD_KT, stream)
@@ -411,9 +467,7 @@ def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
         sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
     if plan.compensated:
         sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
-        sva_attention_compensated(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
-                                  buf.o_r, stream)
-    else:
-        sva_attention(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.o_r, stream)
+    sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o_r,
+                     SVA_LAYOUT_TILE, stream)
     sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
     return buf.o

@@ -62,7 +62,8 @@ struct AttnArgs {
     const int32_t* col;  // [B,H,nnz_per_head]
     const u32x4_t* km;   // block-mean K tiles [B,H,n_mean_groups,d/16,64,8], or NULL
     const u32x4_t* vm;   // block-mean V tiles [B,H,n_mean_groups,4,d,8]
-    uint2* o;            // [B,H,Np,d]
+    uint2* o;            // [B,H,Np,d], or [B,N,H,d] with o_raster
+    int o_raster;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -452,19 +453,31 @@ void attn_kernel(AttnArgs a) {
 #undef SVA_DMA
 #undef SVA_KB
 
-    // epilogue: O = O^T / l, padding query rows zero
+    // epilogue: O = O^T / l.  Tile order: padding query rows are written as
+    // zeros.  Raster order: row qrow goes to raster token inv[qb·BLK + qrow]
+    // (the inverse reorder fused away); padding rows have none.
     const float lt = lane_swap_sum(l);
     const bool row_ok = qrow < p.blk_valid[qb];
     const float inv = (row_ok && lt > 0.f) ? 1.f / lt : 0.f;
-    uint2* op = a.o + ((bh * p.Np) + (int64_t)qb * BLK + qrow) * (D / 4);
+    uint2* op;
+    if (a.o_raster) {
+        if (!row_ok) return;
+        const int n = p.inv[qb * BLK + qrow];
+        const int64_t b = bh / p.H, h = bh - b * p.H;
+        op = a.o + ((b * p.N + n) * p.H + h) * (D / 4);
+    } else {
+        op = a.o + ((bh * p.Np) + (int64_t)qb * BLK + qrow) * (D / 4);
+    }
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             // channels t*32 + 8g + 4hf + 0..3
-            uint2 w;
-            w.x = pack_bf16x2(o[t][4 * g + 0] * inv, o[t][4 * g + 1] * inv);
-            w.y = pack_bf16x2(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+            uint2 w = {0u, 0u};
+            if (row_ok) {
+                w.x = pack_bf16x2(o[t][4 * g + 0] * inv, o[t][4 * g + 1] * inv);
+                w.y = pack_bf16x2(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv);
+            }
             op[(t * 32 + 8 * g + 4 * hf) / 4] = w;
         }
 }
@@ -473,7 +486,7 @@ void attn_kernel(AttnArgs a) {
 
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
                             const uint16_t* vt, const int32_t* col, const uint16_t* km,
-                            const uint16_t* vm, uint16_t* o, hipStream_t s) {
+                            const uint16_t* vm, uint16_t* o, bool o_raster, hipStream_t s) {
     AttnArgs a;
     a.p = p;
     a.q = reinterpret_cast<const u32x4_t*>(qr);
@@ -483,6 +496,7 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
     a.km = reinterpret_cast<const u32x4_t*>(km);
     a.vm = reinterpret_cast<const u32x4_t*>(vm);
     a.o = reinterpret_cast<uint2*>(o);
+    a.o_raster = o_raster ? 1 : 0;
     dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
     dim3 block(p.block * 2);
     const size_t lds = p.dense ? 0

@@ -7,6 +7,9 @@
 // rotate turning channel pairs (2i, 2i+1) of the t/h/w sections by
 // coordinate · theta^(-2i/width) (cos/sin from the plan's tables).
 //
+// The tiled variant writes straight into the attention layouts (Q' in tile
+// order, K' as K tiles), so the separate reorders of Q' and K' disappear.
+//
 // Streaming kernel, bound by HBM: every row is read once and written once
 // (4 · rows · d · 2 bytes for Q and K).  d/8 lanes own one row, 16 bytes
 // each, so a wave moves 1 KB of contiguous rows per access; the sum of
@@ -28,7 +31,11 @@ struct ProArgs {
     const float* w[2];
 };
 
-template <int D>
+// TILED = false: Q', K' in raster order, like the inputs.  TILED = true:
+// straight into the attention layouts, Q' in tile order [B,H,Np,d] and K'
+// as K tiles (the reorders of Q' and K' fused away); the padding rows are
+// zeroed by pad_zero_kernel.
+template <int D, bool TILED>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RPB = kThreads / LPR;        // rows per block per step
@@ -122,7 +129,45 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
             }
             ob[e] = pack_bf16x2(y0 * c - y1 * s, y0 * s + y1 * c);
         }
-        out[(int64_t)row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
+        const u32x4 res = u32x4{ob[0], ob[1], ob[2], ob[3]};
+        if constexpr (!TILED) {
+            out[(int64_t)row * LPR + sub] = res;
+        } else {
+            // tile position of token n of batch b; head h
+            const uint32_t b = fast_div(tok, p.div_N);
+            const int64_t bh = (int64_t)b * p.H + h;
+            const int pos = p.perm[n];
+            if (tensor == 0) {
+                out[(bh * p.Np + pos) * LPR + sub] = res;
+            } else {
+                // K tile entry of token t = pos mod block, 16-byte chunk sub:
+                // group t/32, step sub/2, lane half sub%2, key t%32
+                const int kb = pos / p.block, t = pos - kb * p.block;
+                const int64_t e = ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (D / 16 * 64) +
+                                  (sub >> 1) * 64 + (sub & 1) * 32 + (t & 31);
+                out[e] = res;
+            }
+        }
+    }
+}
+
+// Zero rows of the padding positions [n_video, n_video_pad) of every
+// (b, h): Q' rows in tile order and K'-tile entries.  One workgroup per
+// (b, h), grid.y = tensor.
+template <int D>
+__global__ __launch_bounds__(kThreads) void pad_zero_kernel(DevPlan p, u32x4* qr, u32x4* kt) {
+    constexpr int LPR = D / 8;
+    const int64_t bh = blockIdx.x;
+    const int npad = (int)(p.n_video_pad - p.n_video);
+    for (int i = threadIdx.x; i < npad * LPR; i += kThreads) {
+        const int pos = (int)p.n_video + i / LPR, sub = i % LPR;
+        if (blockIdx.y == 0) {
+            qr[(bh * p.Np + pos) * LPR + sub] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const int kb = pos / p.block, t = pos - kb * p.block;
+            kt[((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (D / 16 * 64) + (sub >> 1) * 64 +
+               (sub & 1) * 32 + (t & 31)] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
@@ -130,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 
 hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
                            const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
-                           hipStream_t s) {
+                           bool tiled, hipStream_t s) {
     ProArgs a;
     a.p = p;
     a.in[0] = q;
@@ -144,10 +189,20 @@ hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* 
     const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
     const int64_t blocks = (rows + per_block - 1) / per_block;
     dim3 grid((unsigned)blocks, 2);
-    if (p.d == 128)
-        hipLaunchKernelGGL(prologue_kernel<128>, grid, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(prologue_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    if (tiled && p.n_video_pad > p.n_video) {
+        dim3 gz((unsigned)((int64_t)p.B * p.H), 2);
+        u32x4* q4 = reinterpret_cast<u32x4*>(qo);
+        u32x4* k4 = reinterpret_cast<u32x4*>(ko);
+        if (p.d == 128) hipLaunchKernelGGL(pad_zero_kernel<128>, gz, dim3(kThreads), 0, s, p, q4, k4);
+        else hipLaunchKernelGGL(pad_zero_kernel<64>, gz, dim3(kThreads), 0, s, p, q4, k4);
+    }
+    if (p.d == 128) {
+        if (tiled) hipLaunchKernelGGL((prologue_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((prologue_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
+    } else {
+        if (tiled) hipLaunchKernelGGL((prologue_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((prologue_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

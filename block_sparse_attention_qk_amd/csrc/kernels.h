@@ -54,9 +54,11 @@ struct DevPlan {
     FastDiv div_H, div_N, div_HW, div_W;
 };
 
+// tiled: qo = Q' in tile order [B,H,Np,d], ko = K' tiles (padding zeroed);
+// otherwise both raster [B,N,H,d]
 hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
                            const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
-                           hipStream_t s);
+                           bool tiled, hipStream_t s);
 
 hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
                           hipStream_t s);
@@ -66,10 +68,11 @@ hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, i
 hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s);
 
-// km, vm: mean tiles (NULL: no compensation)
+// km, vm: mean tiles (NULL: no compensation); o_raster: O in raster order
+// [B,N,H,d] instead of tile order [B,H,Np,d]
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
                             const uint16_t* vt, const int32_t* col, const uint16_t* km,
-                            const uint16_t* vm, uint16_t* o, hipStream_t s);
+                            const uint16_t* vm, uint16_t* o, bool o_raster, hipStream_t s);
 
 hipError_t launch_block_means(const DevPlan& p, const uint16_t* kt, const uint16_t* vt,
                               uint16_t* km, uint16_t* vm, hipStream_t s);

@@ -198,9 +198,28 @@ int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k, const float* w
     hipError_t e = sva::launch_prologue(plan->dev, static_cast<const uint16_t*>(q),
                                         static_cast<const uint16_t*>(k), wq, wk,
                                         static_cast<uint16_t*>(q_out),
-                                        static_cast<uint16_t*>(k_out),
+                                        static_cast<uint16_t*>(k_out), false,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "qk_norm_rope launch");
+    return SVA_OK;
+}
+
+int sva_qk_norm_rope_tiled(sva_plan plan, const void* q, const void* k, const float* wq,
+                           const float* wk, void* q_r, void* k_t, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+    if (!q || !k || !q_r || !k_t)
+        return set_err(SVA_ERR_INVALID_ARG, "q, k, q_r and k_t must be non-NULL");
+    if (!sva::aligned16(q) || !sva::aligned16(k) || !sva::aligned16(q_r) ||
+        !sva::aligned16(k_t) || !sva::aligned16(wq) || !sva::aligned16(wk))
+        return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (q_r == q || q_r == k || k_t == q || k_t == k)
+        return set_err(SVA_ERR_INVALID_ARG, "outputs must not alias the inputs");
+    hipError_t e = sva::launch_prologue(plan->dev, static_cast<const uint16_t*>(q),
+                                        static_cast<const uint16_t*>(k), wq, wk,
+                                        static_cast<uint16_t*>(q_r),
+                                        static_cast<uint16_t*>(k_t), true,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "qk_norm_rope_tiled launch");
     return SVA_OK;
 }
 
@@ -239,23 +258,38 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t, void* wor
     return SVA_OK;
 }
 
-int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
-                  const int32_t* col, void* o_r, void* stream) {
+int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+                     const int32_t* col, const void* km_t, const void* vm_t, void* o,
+                     int o_layout, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
-    if (!q_r || !k_t || !v_t || !o_r)
-        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, v_t and o_r must be non-NULL");
+    if (!q_r || !k_t || !v_t || !o)
+        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, v_t and the output must be non-NULL");
+    if ((km_t == nullptr) != (vm_t == nullptr))
+        return set_err(SVA_ERR_INVALID_ARG, "km_t and vm_t must both be given or both be NULL");
+    if (o_layout != SVA_LAYOUT_TILE && o_layout != SVA_LAYOUT_RASTER)
+        return set_err(SVA_ERR_INVALID_ARG, "unknown output layout");
     if (!plan->host.info.dense && !col)
         return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
     if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(v_t) ||
-        !sva::aligned16(o_r) || ((uintptr_t)col & 3u))
+        !sva::aligned16(o) || !sva::aligned16(km_t) || !sva::aligned16(vm_t) ||
+        ((uintptr_t)col & 3u))
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
     hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
                                          static_cast<const uint16_t*>(k_t),
-                                         static_cast<const uint16_t*>(v_t), col, nullptr,
-                                         nullptr, static_cast<uint16_t*>(o_r),
+                                         static_cast<const uint16_t*>(v_t), col,
+                                         static_cast<const uint16_t*>(km_t),
+                                         static_cast<const uint16_t*>(vm_t),
+                                         static_cast<uint16_t*>(o),
+                                         o_layout == SVA_LAYOUT_RASTER,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "attention launch");
     return SVA_OK;
+}
+
+int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+                  const int32_t* col, void* o_r, void* stream) {
+    return sva_attention_ex(plan, q_r, k_t, v_t, col, nullptr, nullptr, o_r, SVA_LAYOUT_TILE,
+                            stream);
 }
 
 int sva_block_means(sva_plan plan, const void* k_t, const void* v_t, void* km_t, void* vm_t,
@@ -278,25 +312,8 @@ int sva_block_means(sva_plan plan, const void* k_t, const void* v_t, void* km_t,
 int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
                               const void* v_t, const int32_t* col, const void* km_t,
                               const void* vm_t, void* o_r, void* stream) {
-    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
-    if (!q_r || !k_t || !v_t || !o_r || !km_t || !vm_t)
-        return set_err(SVA_ERR_INVALID_ARG,
-                       "q_r, k_t, v_t, km_t, vm_t and o_r must be non-NULL");
-    if (!plan->host.info.dense && !col)
-        return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
-    if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(v_t) ||
-        !sva::aligned16(o_r) || !sva::aligned16(km_t) || !sva::aligned16(vm_t) ||
-        ((uintptr_t)col & 3u))
-        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
-    hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
-                                         static_cast<const uint16_t*>(k_t),
-                                         static_cast<const uint16_t*>(v_t), col,
-                                         static_cast<const uint16_t*>(km_t),
-                                         static_cast<const uint16_t*>(vm_t),
-                                         static_cast<uint16_t*>(o_r),
-                                         static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return sva::hip_err(e, "attention launch");
-    return SVA_OK;
+    if (!km_t || !vm_t) return set_err(SVA_ERR_INVALID_ARG, "km_t and vm_t must be non-NULL");
+    return sva_attention_ex(plan, q_r, k_t, v_t, col, km_t, vm_t, o_r, SVA_LAYOUT_TILE, stream);
 }
 
 const char* sva_status_string(int status) {

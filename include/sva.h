@@ -95,6 +95,11 @@ extern "C" {
 #define SVA_FORWARD_VT  2  /* raster [B,N,H,d] -> V tiles [B,H,nB,block/32,4,d,8] */
 #define SVA_FORWARD_KT  3  /* raster [B,N,H,d] -> K tiles [B,H,nB,block/32,d/16,64,8] */
 
+/* ---- output layouts of sva_attention_ex ---- */
+#define SVA_LAYOUT_TILE    0   /* O in tile order [B, H, Np, d], padding rows zero */
+#define SVA_LAYOUT_RASTER  1   /* O in raster order [B, N, H, d] (the inverse
+                                  reorder fused into the attention)            */
+
 typedef struct sva_plan_s* sva_plan;
 
 /* Full description of a call.  Fill with sva_plan_desc_init() and change
@@ -192,6 +197,15 @@ int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k,
                      const float* wq, const float* wk, void* q_out, void* k_out,
                      void* stream);
 
+/* The same prologue written straight into the layouts the rest of the step
+ * reads (the reorders of Q' and K' fused away): q_r = Q' in tile order
+ * [B, H, Np, d], k_t = K' as K tiles (the layouts of SVA_FORWARD and
+ * SVA_FORWARD_KT), padding rows zero.  Bit-identical to sva_qk_norm_rope
+ * followed by those reorders.  The outputs must not overlap the inputs. */
+int sva_qk_norm_rope_tiled(sva_plan plan, const void* q, const void* k,
+                           const float* wq, const float* wk, void* q_r, void* k_t,
+                           void* stream);
+
 /* Token permutation between raster and 3D-tile order (see direction
  * macros).  Forward writes zeros into the padding rows; the inverse drops
  * them.  `in` and `out` must not overlap. */
@@ -242,6 +256,15 @@ int sva_block_means(sva_plan plan, const void* k_t, const void* v_t, void* km_t,
 int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
                               const void* v_t, const int32_t* col, const void* km_t,
                               const void* vm_t, void* o_r, void* stream);
+
+/* General attention entry: km_t, vm_t both NULL (sva_attention) or both the
+ * mean tiles of sva_block_means (sva_attention_compensated); o_layout
+ * SVA_LAYOUT_TILE writes O like sva_attention, SVA_LAYOUT_RASTER writes
+ * it in raster order [B, N, H, d], bit-identical to SVA_INVERSE of the
+ * tile-order output. */
+int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+                     const int32_t* col, const void* km_t, const void* vm_t, void* o,
+                     int o_layout, void* stream);
 
 /* ---- errors ---- */
 const char* sva_status_string(int status);

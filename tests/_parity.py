@@ -148,9 +148,18 @@ class GpuRun:
         self.wk = torch.from_numpy(np.ascontiguousarray(wk)).cuda()
 
     def run(self):
-        S.forward(self.plan, self.q, self.k, self.v, self.wq, self.wk, self.buf)
+        """The step one call per stage; every intermediate stays in buf."""
+        S.forward_staged(self.plan, self.q, self.k, self.v, self.wq, self.wk, self.buf)
         torch.cuda.synchronize()
         return self
+
+    def run_fused(self):
+        """The fused step (tiled prologue, raster attention output) into a
+        fresh set of buffers; returns them."""
+        buf = S.Buffers(self.plan)
+        S.forward(self.plan, self.q, self.k, self.v, self.wq, self.wk, buf)
+        torch.cuda.synchronize()
+        return buf
 
 
 def workload_inputs(wl):

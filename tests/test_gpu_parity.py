@@ -237,6 +237,45 @@ def dev_col(col_np):
     return torch.from_numpy(col_np).cuda()
 
 
+_NAN_BITS = 0x7FC0   # bf16 quiet NaN: a stale value would show
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_tiled_prologue_is_prologue_plus_reorders(name):
+    """sva_qk_norm_rope_tiled equals sva_qk_norm_rope followed by the Q'
+    and K' reorders, bit for bit, padding included."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    S.sva_qk_norm_rope(run.plan, run.q, run.k, run.wq, run.wk, run.buf.qn, run.buf.kn)
+    S.sva_reorder(run.plan, run.buf.qn, run.buf.q_r, S.SVA_FORWARD)
+    S.sva_reorder(run.plan, run.buf.kn, run.buf.k_t, S.SVA_FORWARD_KT)
+    qr_t = torch.full(run.plan.tile_shape, 0, dtype=torch.int16, device="cuda")
+    kt_t = torch.full(run.plan.kt_shape, 0, dtype=torch.int16, device="cuda")
+    qr_t.fill_(_NAN_BITS)
+    kt_t.fill_(_NAN_BITS)
+    qr_t, kt_t = qr_t.view(torch.bfloat16), kt_t.view(torch.bfloat16)
+    S.sva_qk_norm_rope_tiled(run.plan, run.q, run.k, run.wq, run.wk, qr_t, kt_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qr_t), host(run.buf.q_r))
+    assert np.array_equal(host(kt_t), host(run.buf.k_t))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_raster_output_is_inverse_reorder(name):
+    """sva_attention_ex with the raster layout equals the tile-order output
+    followed by SVA_INVERSE, bit for bit."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk).run()
+    o_ras = torch.full(run.plan.raster_shape, 0, dtype=torch.int16, device="cuda")
+    o_ras.fill_(_NAN_BITS)
+    o_ras = o_ras.view(torch.bfloat16)
+    b = run.buf
+    S.sva_attention_ex(run.plan, b.q_r, b.k_t, b.v_t, b.col, b.km_t, b.vm_t, o_ras,
+                       S.SVA_LAYOUT_RASTER)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o_ras), host(b.o))
+
+
 @pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].flags & I.COMPENSATE])
 def test_block_means_parity(name):
     """Mean tiles: every block's mean key and value within one bf16 step of
@@ -292,6 +331,11 @@ def test_chained_parity(name):
             diffs += int((kept != r["kept"]).sum())
     print(f"{name}: chained rel_l2 {worst_rel:.2e} max_abs {worst_abs:.2e} mask diffs {diffs}")
     assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
+    # the fused step computes the same bits
+    fb = run.run_fused()
+    assert np.array_equal(host(fb.o), host(run.buf.o))
+    if not run.plan.info.dense:
+        assert np.array_equal(fb.col.cpu().numpy(), run.buf.col.cpu().numpy())
 
 
 @pytest.mark.parametrize("name", ["ragged128", "tiny"])
@@ -422,6 +466,10 @@ def test_full_workload_sampled(name):
         stats["chain_mask_diffs"] += int((r["kept"] != kept_g).sum())
         worst["ch_rel"] = max(worst["ch_rel"], rel_l2(o_g[rows], r["o_r"][rows]))
         worst["ch_abs"] = max(worst["ch_abs"], max_abs(o_g[rows], r["o_r"][rows]))
+    fb = run.run_fused()
+    if not torch.equal(fb.o.view(torch.int16), run.buf.o.view(torch.int16)):
+        fails.append(("fused step differs from the staged step",))
+    del fb
     print(f"{name}: heads {heads} qblocks {qbs} {stats} {worst}", flush=True)
     assert not fails, fails
     assert stats["ulp_mism"] <= 1e-3 * stats["elems"]
