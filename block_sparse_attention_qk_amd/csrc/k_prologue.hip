@@ -24,6 +24,25 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 4;   // rows per thread
 
+// The arithmetic of one row, with every rounding explicit so that the
+// raster and the tiled kernels produce the same bits.  HIP's __fmul_rn and
+// friends are plain operators here, so contraction into FMA is switched off
+// in these helpers: otherwise the compiler may fuse a product into the
+// following add differently in each kernel.
+__device__ __forceinline__ float rms_scale(float ss, float inv_d, float eps) {
+    return rsqrtf(__fmaf_rn(ss, inv_d, eps));
+}
+__device__ __forceinline__ float norm_val(float v, float rs, float w) {
+#pragma clang fp contract(off)
+    return (v * rs) * w;
+}
+__device__ __forceinline__ uint32_t rotate_pair(uint32_t yb, float c, float s) {
+#pragma clang fp contract(off)
+    const float y0 = bf16lo(yb), y1 = bf16hi(yb);
+    const float a = y0 * c, b = y1 * s, e = y0 * s, f = y1 * c;
+    return pack_bf16x2(a - b, e + f);
+}
+
 struct ProArgs {
     DevPlan p;
     const uint16_t* in[2];
@@ -31,11 +50,7 @@ struct ProArgs {
     const float* w[2];
 };
 
-// TILED = false: Q', K' in raster order, like the inputs.  TILED = true:
-// straight into the attention layouts, Q' in tile order [B,H,Np,d] and K'
-// as K tiles (the reorders of Q' and K' fused away); the padding rows are
-// zeroed by pad_zero_kernel.
-template <int D, bool TILED>
+template <int D>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RPB = kThreads / LPR;        // rows per block per step
@@ -94,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
         const uint32_t tok = fast_div(row, p.div_H);
         const uint32_t h = row - tok * (uint32_t)p.H;
         const uint32_t n = tok - fast_div(tok, p.div_N) * (uint32_t)p.N;
-        const float rs = rsqrtf(ss * inv_d + p.eps);
+        const float rs = rms_scale(ss, inv_d, p.eps);
         float wv[8];
         if (w) {
             const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
@@ -109,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
         uint32_t yb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            yb[e] = pack_bf16x2(v[2 * e] * rs * wv[2 * e], v[2 * e + 1] * rs * wv[2 * e + 1]);
+            yb[e] = pack_bf16x2(norm_val(v[2 * e], rs, wv[2 * e]),
+                                norm_val(v[2 * e + 1], rs, wv[2 * e + 1]));
         // grid coordinates (t, h, w) of a video token; extra tokens get none
         const bool video = n < (uint32_t)p.n_video;
         const uint32_t pt = fast_div(n, p.div_HW);
@@ -119,7 +135,6 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
         uint32_t ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float y0 = bf16lo(yb[e]), y1 = bf16hi(yb[e]);
             float c = 1.f, s = 0.f;
             if (video && pax[e] >= 0) {
                 const uint32_t pos = pax[e] == 0 ? pt : (pax[e] == 1 ? ph : pw);
@@ -127,47 +142,178 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
                 c = cs.x;
                 s = cs.y;
             }
-            ob[e] = pack_bf16x2(y0 * c - y1 * s, y0 * s + y1 * c);
+            ob[e] = rotate_pair(yb[e], c, s);
         }
-        const u32x4 res = u32x4{ob[0], ob[1], ob[2], ob[3]};
-        if constexpr (!TILED) {
-            out[(int64_t)row * LPR + sub] = res;
-        } else {
-            // tile position of token n of batch b; head h
-            const uint32_t b = fast_div(tok, p.div_N);
-            const int64_t bh = (int64_t)b * p.H + h;
-            const int pos = p.perm[n];
-            if (tensor == 0) {
-                out[(bh * p.Np + pos) * LPR + sub] = res;
-            } else {
-                // K tile entry of token t = pos mod block, 16-byte chunk sub:
-                // group t/32, step sub/2, lane half sub%2, key t%32
-                const int kb = pos / p.block, t = pos - kb * p.block;
-                const int64_t e = ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (D / 16 * 64) +
-                                  (sub >> 1) * 64 + (sub & 1) * 32 + (t & 31);
-                out[e] = res;
-            }
-        }
+        out[(int64_t)row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
     }
 }
 
-// Zero rows of the padding positions [n_video, n_video_pad) of every
-// (b, h): Q' rows in tile order and K'-tile entries.  One workgroup per
-// (b, h), grid.y = tensor.
-template <int D>
-__global__ __launch_bounds__(kThreads) void pad_zero_kernel(DevPlan p, u32x4* qr, u32x4* kt) {
-    constexpr int LPR = D / 8;
-    const int64_t bh = blockIdx.x;
-    const int npad = (int)(p.n_video_pad - p.n_video);
-    for (int i = threadIdx.x; i < npad * LPR; i += kThreads) {
-        const int pos = (int)p.n_video + i / LPR, sub = i % LPR;
-        if (blockIdx.y == 0) {
-            qr[(bh * p.Np + pos) * LPR + sub] = u32x4{0u, 0u, 0u, 0u};
-        } else {
-            const int kb = pos / p.block, t = pos - kb * p.block;
-            kt[((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (D / 16 * 64) + (sub >> 1) * 64 +
-               (sub & 1) * 32 + (t & 31)] = u32x4{0u, 0u, 0u, 0u};
+// The prologue written straight into the attention layouts.  A workgroup
+// owns one 32-position group of the tile order (one K-tile group) for HG
+// consecutive heads of one batch; position pos holds raster token inv[pos]
+// (or padding).  Row R of the workgroup is (position R / HG, head R % HG),
+// so the rows a wave loads together are neighbouring heads of one token:
+// HG · d · 2 contiguous bytes of [B, N, H, d] instead of scattered d · 2
+// byte pieces.  Rows are loaded and computed exactly as in the raster kernel
+// (d/8 lanes per row, all of a thread's rows loaded before any is used;
+// HG divides the rows per pass, so a thread keeps one head), then
+//  Q' (KT = false): written as tile-order rows, 32 consecutive per head;
+//  K' (KT = true): staged in LDS (row stride padded by 16 bytes so the
+//     column reads below are free of bank conflicts) and written as K tiles:
+//     wave g owns heads g, g + 4, ..; lane 32·hf + j reads chunk 2s + hf of
+//     token j, so every step s writes one contiguous 1 KB span.
+// Padding positions (no raster token) are written as zeros.
+constexpr int kTileHeads = 4;   // HG
+
+template <int D, bool KT>
+__global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
+    constexpr int HG = kTileHeads;
+    constexpr int LPR = D / 8;                 // 16-byte chunks (lanes) per row
+    constexpr int DS = D / 16;                 // K-tile steps (chunk pairs)
+    constexpr int RPP = kThreads / LPR;        // rows per pass
+    constexpr int NP = 32 * HG / RPP;          // rows per thread
+    constexpr int LS = LPR + 1;                // LDS row stride in chunks
+    static_assert(RPP % HG == 0, "a thread must keep one head");
+    __shared__ u32x4 stage[KT ? 32 * HG * LS : 1];
+    const int tensor = KT ? 1 : 0;
+    const DevPlan& p = a.p;
+    const u32x4* in = reinterpret_cast<const u32x4*>(a.in[tensor]);
+    u32x4* out = reinterpret_cast<u32x4*>(a.out[tensor]);
+    const float* __restrict__ w = a.w[tensor];
+    const int ngroups = (int)(p.Np / 32);      // Np is a multiple of 32
+    const int nhg = (p.H + HG - 1) / HG;
+    const int64_t b = blockIdx.x / ((int64_t)ngroups * nhg);
+    const int rest = (int)(blockIdx.x - b * ((int64_t)ngroups * nhg));
+    const int grp = rest / nhg;
+    const int h0 = (rest - grp * nhg) * HG;
+    const int pos0 = grp * 32;
+    const int sub = threadIdx.x % LPR;
+    const int r0 = threadIdx.x / LPR;
+    const int h = h0 + r0 % HG;               // this thread's head
+    const bool hok = h < p.H;
+    const uint32_t hw = (uint32_t)(p.Hh * p.W);
+
+    // Loads in three branch-free batches (token index, row, cos/sin), each
+    // address clamped to a valid one and the value discarded afterwards
+    // where the row does not exist, so that a batch is in flight at once.
+    const int hc = hok ? h : 0;
+    float wv[8];   // issued first: the first row needs them
+    if (w) {
+        const float4* wp = reinterpret_cast<const float4*>(w + hc * D + sub * 8);
+        const float4 w0 = wp[0], w1 = wp[1];
+        wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = 1.f;
+    }
+    int nr[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int n = p.inv[pos0 + (r0 + i * RPP) / HG];   // Np is a multiple of 32
+        nr[i] = hok ? n : -2;                 // -2: no such head, -1: padding
+    }
+    u32x4 x[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int n = nr[i] >= 0 ? nr[i] : 0;
+        x[i] = in[((b * p.N + n) * p.H + hc) * LPR + sub];
+    }
+    // this lane's channel pairs: RoPE section (-1: none), offset in its
+    // table and the section's width
+    int pax[4], pbase[4], phalf[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int pi = sub * 4 + e;
+        pax[e] = -1;
+        pbase[e] = 0;
+        phalf[e] = 0;
+#pragma unroll
+        for (int ax = 0; ax < 3; ++ax) {
+            const int half = p.rope_half[ax];
+            if (pax[e] < 0 && pi < half) {
+                pax[e] = ax;
+                pbase[e] = p.rope_off[ax] + pi;
+                phalf[e] = half;
+            }
+            pi -= half;
         }
+    }
+    // every row's cos/sin (the table always holds entry 0, the identity
+    // rotation is substituted where a pair is not rotated)
+    float2 cs[NP][4];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int n = nr[i];
+        const bool video = n >= 0 && n < p.n_video;
+        const uint32_t un = video ? (uint32_t)n : 0u;
+        const uint32_t pt = fast_div(un, p.div_HW);
+        const uint32_t rem = un - pt * hw;
+        const uint32_t ph = fast_div(rem, p.div_W);
+        const uint32_t pw = rem - ph * (uint32_t)p.W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t gp = pax[e] == 0 ? pt : (pax[e] == 1 ? ph : pw);
+            const bool rot = video && pax[e] >= 0;
+            cs[i][e] = p.rope_cs[rot ? pbase[e] + gp * (uint32_t)phalf[e] : 0u];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const bool valid = nr[i] >= 0;
+        x[i] = valid ? x[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool rot = valid && nr[i] < p.n_video && pax[e] >= 0;
+            cs[i][e] = rot ? cs[i][e] : make_float2(1.f, 0.f);
+        }
+    }
+    const float inv_d = 1.0f / D;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int r = r0 + i * RPP;
+        const int n = nr[i];
+        const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16lo(u[e]);
+            v[2 * e + 1] = bf16hi(u[e]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+        u32x4 res = u32x4{0u, 0u, 0u, 0u};
+        if (n >= 0) {
+            const float rs = rms_scale(ss, inv_d, p.eps);
+            uint32_t ob[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t yb = pack_bf16x2(norm_val(v[2 * e], rs, wv[2 * e]),
+                                                norm_val(v[2 * e + 1], rs, wv[2 * e + 1]));
+                ob[e] = rotate_pair(yb, cs[i][e].x, cs[i][e].y);
+            }
+            res = u32x4{ob[0], ob[1], ob[2], ob[3]};
+        }
+        if constexpr (KT) {
+            stage[r * LS + sub] = res;
+        } else {
+            if (hok) out[(((b * p.H + h) * p.Np) + pos0 + r / HG) * LPR + sub] = res;
+        }
+    }
+    if constexpr (!KT) return;
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 31, hf = lane >> 5;
+    const int kb = pos0 / p.block, t = pos0 - kb * p.block;
+    for (int hl = threadIdx.x >> 6; hl < HG; hl += kThreads / 64) {
+        if (h0 + hl >= p.H) break;
+        const int64_t bh = b * p.H + h0 + hl;
+        u32x4* dst = out + ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (DS * 64) + lane;
+#pragma unroll
+        for (int s2 = 0; s2 < DS; ++s2) dst[s2 * 64] = stage[(j * HG + hl) * LS + 2 * s2 + hf];
     }
 }
 
@@ -188,21 +334,23 @@ hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* 
     const int lpr = p.d / 8;
     const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
     const int64_t blocks = (rows + per_block - 1) / per_block;
+    if (tiled) {
+        const int64_t nhg = (p.H + kTileHeads - 1) / kTileHeads;
+        dim3 gt((unsigned)((int64_t)p.B * (p.Np / 32) * nhg));
+        if (p.d == 128) {
+            hipLaunchKernelGGL((prologue_tiled_kernel<128, false>), gt, dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((prologue_tiled_kernel<128, true>), gt, dim3(kThreads), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((prologue_tiled_kernel<64, false>), gt, dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((prologue_tiled_kernel<64, true>), gt, dim3(kThreads), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)blocks, 2);
-    if (tiled && p.n_video_pad > p.n_video) {
-        dim3 gz((unsigned)((int64_t)p.B * p.H), 2);
-        u32x4* q4 = reinterpret_cast<u32x4*>(qo);
-        u32x4* k4 = reinterpret_cast<u32x4*>(ko);
-        if (p.d == 128) hipLaunchKernelGGL(pad_zero_kernel<128>, gz, dim3(kThreads), 0, s, p, q4, k4);
-        else hipLaunchKernelGGL(pad_zero_kernel<64>, gz, dim3(kThreads), 0, s, p, q4, k4);
-    }
-    if (p.d == 128) {
-        if (tiled) hipLaunchKernelGGL((prologue_kernel<128, true>), grid, dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((prologue_kernel<128, false>), grid, dim3(kThreads), 0, s, a);
-    } else {
-        if (tiled) hipLaunchKernelGGL((prologue_kernel<64, true>), grid, dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((prologue_kernel<64, false>), grid, dim3(kThreads), 0, s, a);
-    }
+    if (p.d == 128)
+        hipLaunchKernelGGL(prologue_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(prologue_kernel<64>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
