@@ -64,29 +64,75 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
     const uint32_t rows = (uint32_t)(p.B * p.N * p.H);
     const uint32_t row0 = blockIdx.x * (uint32_t)(RPB * kRows) + threadIdx.x / LPR;
 
+    // Loads go out in branch-free batches (rows, weights, cos/sin) from
+    // addresses clamped to the last row, so a thread's loads are in flight
+    // together; past-the-end rows are computed and not stored.
     u32x4 x[kRows];
+    uint32_t hr[kRows], nr[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const uint32_t row = row0 + r * RPB;
-        x[r] = row < rows ? in[(int64_t)row * LPR + sub] : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t row = min(row0 + r * RPB, rows - 1);
+        x[r] = in[(int64_t)row * LPR + sub];
+        const uint32_t tok = fast_div(row, p.div_H);
+        hr[r] = row - tok * (uint32_t)p.H;
+        nr[r] = tok - fast_div(tok, p.div_N) * (uint32_t)p.N;
+    }
+    float wv[kRows][8];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        if (w) {
+            const float4* wp = reinterpret_cast<const float4*>(w + hr[r] * D + sub * 8);
+            const float4 w0 = wp[0], w1 = wp[1];
+            wv[r][0] = w0.x; wv[r][1] = w0.y; wv[r][2] = w0.z; wv[r][3] = w0.w;
+            wv[r][4] = w1.x; wv[r][5] = w1.y; wv[r][6] = w1.z; wv[r][7] = w1.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[r][e] = 1.f;
+        }
     }
 
-    // this lane's four channel pairs: RoPE section (-1: not rotated) and the
-    // pair's offset in that section's cos/sin table
-    int pax[4], pbase[4];
+    // this lane's four channel pairs: RoPE section (-1: not rotated), the
+    // pair's offset in that section's cos/sin table and the section's width
+    int pax[4], pbase[4], phalf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         int pi = sub * 4 + e;
         pax[e] = -1;
         pbase[e] = 0;
+        phalf[e] = 0;
 #pragma unroll
         for (int ax = 0; ax < 3; ++ax) {
             const int half = p.rope_half[ax];
             if (pax[e] < 0 && pi < half) {
                 pax[e] = ax;
                 pbase[e] = p.rope_off[ax] + pi;
+                phalf[e] = half;
             }
             pi -= half;
+        }
+    }
+    // cos/sin of every row's pairs (grid coordinates (t, h, w) of a video
+    // token; extra tokens and pairs past the sections are not rotated; the
+    // table always holds entry 0)
+    float2 cs[kRows][4];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const bool video = nr[r] < (uint32_t)p.n_video;
+        const uint32_t n = video ? nr[r] : 0u;
+        const uint32_t pt = fast_div(n, p.div_HW);
+        const uint32_t rem = n - pt * (uint32_t)(p.Hh * p.W);
+        const uint32_t ph = fast_div(rem, p.div_W);
+        const uint32_t pw = rem - ph * (uint32_t)p.W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t gp = pax[e] == 0 ? pt : (pax[e] == 1 ? ph : pw);
+            const bool rot = video && pax[e] >= 0;
+            cs[r][e] = p.rope_cs[rot ? pbase[e] + gp * (uint32_t)phalf[e] : 0u];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool rot = video && pax[e] >= 0;
+            cs[r][e] = rot ? cs[r][e] : make_float2(1.f, 0.f);
         }
     }
     const float inv_d = 1.0f / D;
@@ -105,46 +151,17 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
         for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
 #pragma unroll
         for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-        if (row >= rows) continue;
-        const uint32_t tok = fast_div(row, p.div_H);
-        const uint32_t h = row - tok * (uint32_t)p.H;
-        const uint32_t n = tok - fast_div(tok, p.div_N) * (uint32_t)p.N;
         const float rs = rms_scale(ss, inv_d, p.eps);
-        float wv[8];
-        if (w) {
-            const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
-            const float4 w0 = wp[0], w1 = wp[1];
-            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wv[e] = 1.f;
-        }
-        // norm, then round to bf16 (the stored value the rotation starts from)
-        uint32_t yb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            yb[e] = pack_bf16x2(norm_val(v[2 * e], rs, wv[2 * e]),
-                                norm_val(v[2 * e + 1], rs, wv[2 * e + 1]));
-        // grid coordinates (t, h, w) of a video token; extra tokens get none
-        const bool video = n < (uint32_t)p.n_video;
-        const uint32_t pt = fast_div(n, p.div_HW);
-        const uint32_t rem = n - pt * (uint32_t)(p.Hh * p.W);
-        const uint32_t ph = fast_div(rem, p.div_W);
-        const uint32_t pw = rem - ph * (uint32_t)p.W;
+        // norm, round to bf16 (the stored value the rotation starts from),
+        // rotate
         uint32_t ob[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float c = 1.f, s = 0.f;
-            if (video && pax[e] >= 0) {
-                const uint32_t pos = pax[e] == 0 ? pt : (pax[e] == 1 ? ph : pw);
-                const float2 cs = p.rope_cs[pbase[e] + pos * p.rope_half[pax[e]]];
-                c = cs.x;
-                s = cs.y;
-            }
-            ob[e] = rotate_pair(yb[e], c, s);
+            const uint32_t yb = pack_bf16x2(norm_val(v[2 * e], rs, wv[r][2 * e]),
+                                            norm_val(v[2 * e + 1], rs, wv[r][2 * e + 1]));
+            ob[e] = rotate_pair(yb, cs[r][e].x, cs[r][e].y);
         }
-        out[(int64_t)row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
+        if (row < rows) out[(int64_t)row * LPR + sub] = u32x4{ob[0], ob[1], ob[2], ob[3]};
     }
 }
 

@@ -27,63 +27,68 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 4;
 
-// Forward: one output row (b, h, p) per d/8 lanes.
+// Forward: one output row (b, h, p) per d/8 lanes.  Loads go out in
+// branch-free batches (token indices, then rows from clamped addresses),
+// so a thread's rows are in flight together; the row index is below 2^31.
 template <int D>
 __global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const u32x4* in,
                                                                u32x4* out) {
     constexpr int LPR = D / 8;
     constexpr int RPB = kThreads / LPR;
     const int sub = threadIdx.x % LPR;
-    const int64_t rows = (int64_t)p.B * p.H * p.Np;
-    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
-    u32x4 v[kRows];
-    int64_t dst[kRows];
+    const uint32_t rows = (uint32_t)(p.B * p.H * p.Np);
+    const uint32_t row0 = blockIdx.x * (uint32_t)(RPB * kRows) + threadIdx.x / LPR;
+    int n[kRows];
+    uint32_t bh[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const int64_t row = row0 + (int64_t)r * RPB;
-        dst[r] = row;
-        v[r] = u32x4{0u, 0u, 0u, 0u};
-        if (row < rows) {
-            const int64_t pos = row % p.Np;
-            const int64_t bh = row / p.Np;
-            const int h = (int)(bh % p.H);
-            const int64_t b = bh / p.H;
-            const int n = p.inv[pos];
-            if (n >= 0) v[r] = in[((b * p.N + n) * p.H + h) * LPR + sub];
-        }
+        const uint32_t row = min(row0 + r * RPB, rows - 1);
+        bh[r] = fast_div(row, p.div_Np);
+        n[r] = p.inv[row - bh[r] * (uint32_t)p.Np];
+    }
+    u32x4 v[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const uint32_t b = fast_div(bh[r], p.div_H);
+        const uint32_t h = bh[r] - b * (uint32_t)p.H;
+        const int64_t src = ((int64_t)b * p.N + (n[r] >= 0 ? n[r] : 0)) * p.H + h;
+        v[r] = in[src * LPR + sub];
     }
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-        if (dst[r] < rows) out[dst[r] * LPR + sub] = v[r];
+    for (int r = 0; r < kRows; ++r) {
+        const uint32_t row = row0 + r * RPB;
+        if (row < rows) out[(int64_t)row * LPR + sub] = n[r] >= 0 ? v[r] : u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // Inverse: one output raster row (b, n, h) per d/8 lanes; writes are
-// contiguous, reads gather whole rows.
+// contiguous, reads gather whole rows (batched as in the forward kernel).
 template <int D>
 __global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const u32x4* in,
                                                                u32x4* out) {
     constexpr int LPR = D / 8;
     constexpr int RPB = kThreads / LPR;
     const int sub = threadIdx.x % LPR;
-    const int64_t rows = (int64_t)p.B * p.N * p.H;
-    const int64_t row0 = (int64_t)blockIdx.x * RPB * kRows + threadIdx.x / LPR;
+    const uint32_t rows = (uint32_t)(p.B * p.N * p.H);
+    const uint32_t row0 = blockIdx.x * (uint32_t)(RPB * kRows) + threadIdx.x / LPR;
+    int pos[kRows];
+    uint32_t bh[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const uint32_t row = min(row0 + r * RPB, rows - 1);
+        const uint32_t bn = fast_div(row, p.div_H);
+        const uint32_t h = row - bn * (uint32_t)p.H;
+        const uint32_t b = fast_div(bn, p.div_N);
+        pos[r] = p.perm[bn - b * (uint32_t)p.N];
+        bh[r] = b * (uint32_t)p.H + h;
+    }
     u32x4 v[kRows];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        const int64_t row = row0 + (int64_t)r * RPB;
-        if (row < rows) {
-            const int h = (int)(row % p.H);
-            const int64_t bn = row / p.H;
-            const int64_t n = bn % p.N;
-            const int64_t b = bn / p.N;
-            const int64_t pos = p.perm[n];
-            v[r] = in[((b * p.H + h) * p.Np + pos) * LPR + sub];
-        }
-    }
+    for (int r = 0; r < kRows; ++r) v[r] = in[((int64_t)bh[r] * p.Np + pos[r]) * LPR + sub];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const int64_t row = row0 + (int64_t)r * RPB;
-        if (row < rows) out[row * LPR + sub] = v[r];
+        const uint32_t row = row0 + r * RPB;
+        if (row < rows) out[(int64_t)row * LPR + sub] = v[r];
     }
 }
 
@@ -110,14 +115,18 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
     const int h = (int)(bh % p.H);
     const int64_t b = bh / p.H;
     const int key0 = 16 * (kg >> 1) + 4 * (kg & 1);
+    // branch-free batches: the 8 token indices, then the 8 rows (padding
+    // reads token 0 and is zeroed afterwards)
+    int n[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) n[j] = p.inv[kb * BLK + key0 + (j & 3) + 8 * (j >> 2)];
+    u32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = in[((b * p.N + (n[j] >= 0 ? n[j] : 0)) * p.H + h) * DC + dc];
     uint32_t m[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int key = key0 + (j & 3) + 8 * (j >> 2);
-        const int64_t pos = (int64_t)kb * BLK + key;
-        const int n = p.inv[pos];
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (n >= 0) v = in[((b * p.N + n) * p.H + h) * DC + dc];
+        const u32x4 v = n[j] >= 0 ? x[j] : u32x4{0u, 0u, 0u, 0u};
         m[j][0] = v.x; m[j][1] = v.y; m[j][2] = v.z; m[j][3] = v.w;
     }
     // 32-key group kg/4, chunk kg%4: d rows of 8 keys
@@ -149,17 +158,24 @@ __global__ __launch_bounds__(256) void reorder_kt_kernel(DevPlan p, const u32x4*
     const int h = (int)(bh % p.H);
     const int64_t b = bh / p.H;
     u32x4* dst = out + (bh * p.nB + kb) * (int64_t)CHUNKS;
+    constexpr int NI = CHUNKS / 256;
+    // branch-free batches as in the V-tile kernel
+    int n[NI];
 #pragma unroll
-    for (int i = 0; i < CHUNKS / 256; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int q = threadIdx.x + i * 256;   // (g, s, hf, j) with j fastest
-        const int j = q & 31, hf = (q >> 5) & 1, s = (q >> 6) % (D / 16);
         const int g = (q >> 6) / (D / 16);
-        const int64_t pos = (int64_t)kb * BLK + g * 32 + j;
-        const int n = p.inv[pos];
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (n >= 0) v = in[((b * p.N + n) * p.H + h) * DC + 2 * s + hf];
-        dst[q] = v;
+        n[i] = p.inv[kb * BLK + g * 32 + (q & 31)];
     }
+    u32x4 x[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int q = threadIdx.x + i * 256;
+        const int hf = (q >> 5) & 1, s = (q >> 6) % (D / 16);
+        x[i] = in[((b * p.N + (n[i] >= 0 ? n[i] : 0)) * p.H + h) * DC + 2 * s + hf];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dst[threadIdx.x + i * 256] = n[i] >= 0 ? x[i] : u32x4{0u, 0u, 0u, 0u};
 }
 
 }  // namespace

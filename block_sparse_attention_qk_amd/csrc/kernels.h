@@ -51,7 +51,7 @@ struct DevPlan {
     int64_t nnz_per_head;
     int max_row_len;
     // divisions of (token, head) row indices, all below 2^31
-    FastDiv div_H, div_N, div_HW, div_W;
+    FastDiv div_H, div_N, div_HW, div_W, div_Np;
 };
 
 // tiled: qo = Q' in tile order [B,H,Np,d], ko = K' tiles (padding zeroed);

@@ -161,6 +161,7 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.div_N = sva::make_fastdiv((uint32_t)I.N);
     d.div_HW = sva::make_fastdiv((uint32_t)(ds.Hh * ds.W));
     d.div_W = sva::make_fastdiv((uint32_t)ds.W);
+    d.div_Np = sva::make_fastdiv((uint32_t)I.Np);
     *out = plan;
     return SVA_OK;
 }
