@@ -105,13 +105,18 @@ def main():
             S.sva_reorder(plan, buf.kn, buf.k_t, S.SVA_FORWARD_KT)
             rec()
         else:
-            # fused: the prologue writes Q' in tile order and K' as K tiles
-            S.sva_qk_norm_rope_tiled(plan, dq, dk, dwq, dwk, buf.q_r, buf.k_t)
+            # fused: the prologue writes Q' in tile order, K' as K tiles and
+            # the block means the selection ranks
+            S.sva_qk_norm_rope_tiled(plan, dq, dk, dwq, dwk, buf.q_r, buf.k_t,
+                                     None if info.dense else buf.ws)
             rec()
         S.sva_reorder(plan, dv, buf.v_t, S.SVA_FORWARD_VT)
         rec()
         if not info.dense:
-            S.sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col)
+            if args.staged:
+                S.sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col)
+            else:
+                S.sva_select_blocks(plan, None, None, buf.ws, buf.col)
         rec()
         if plan.compensated:
             S.sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t)
@@ -175,7 +180,8 @@ def main():
     if args.staged:
         stage_gbs["reorder_qk"] = 2 * (B * H * (N + Np) * d * 2) / (stage["reorder_qk"] * 1e-3) / 1e9
         stage_gbs["reorder_o"] = (B * H * (N + Np) * d * 2) / (stage["reorder_o"] * 1e-3) / 1e9
-    if not info.dense:
+    if not info.dense and args.staged:
+        # the fused path pools inside the prologue; its select only ranks
         stage_gbs["select"] = sel_bytes / (stage["select"] * 1e-3) / 1e9
 
     out = {

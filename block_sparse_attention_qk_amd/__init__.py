@@ -109,7 +109,7 @@ def lib() -> ctypes.CDLL:
     L.sva_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.sva_block_means.argtypes = [vp, vp, vp, vp, vp, vp]
     L.sva_attention_compensated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    L.sva_qk_norm_rope_tiled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sva_qk_norm_rope_tiled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.sva_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
@@ -300,7 +300,18 @@ def sva_qk_norm_rope(plan: Plan, q, k, wq, wk, q_out, k_out, stream=None) -> Non
     _check(lib().sva_qk_norm_rope(plan.handle, *args, _stream(stream)))
 
 
-def sva_qk_norm_rope_tiled(plan: Plan, q, k, wq, wk, q_r, k_t, stream=None) -> None:
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def sva_qk_norm_rope_tiled(plan: Plan, q, k, wq, wk, q_r, k_t, workspace=None,
+                           stream=None) -> None:
+    """Tiled prologue; with ``workspace`` (the select workspace) it also
+    writes the block means sva_select_blocks(q_r=None, k_t=None) ranks."""
     import torch
     shp = plan.raster_shape
     wshape = (plan.desc.H, plan.desc.d)
@@ -311,7 +322,8 @@ def sva_qk_norm_rope_tiled(plan: Plan, q, k, wq, wk, q_r, k_t, stream=None) -> N
         _tensor(q_r, plan.tile_shape, torch.bfloat16, "q_r"),
         _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
     ]
-    _check(lib().sva_qk_norm_rope_tiled(plan.handle, *args, _stream(stream)))
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().sva_qk_norm_rope_tiled(plan.handle, *args, ws, ws_bytes, _stream(stream)))
 
 
 def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
@@ -331,18 +343,19 @@ def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
 
 
 def sva_select_blocks(plan: Plan, q_r, k_t, workspace, col, stream=None) -> None:
+    """q_r = k_t = None: rank the means the tiled prologue left in
+    ``workspace``."""
     import torch
     if plan.info.dense:
         return
     ts = plan.tile_shape
-    if not (workspace.is_cuda and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous GPU tensor")
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().sva_select_blocks(plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r"),
-                                   _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
-                                   ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
-                                   _tensor(col, (int(plan.info.nnz),), torch.int32, "col"),
-                                   _stream(stream)))
+    if workspace is None:
+        raise ValueError("workspace is required")
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().sva_select_blocks(
+        plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r") if q_r is not None else None,
+        _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t") if k_t is not None else None,
+        ws, ws_bytes, _tensor(col, (int(plan.info.nnz),), torch.int32, "col"), _stream(stream)))
 
 
 def sva_attention(plan: Plan, q_r, k_t, v_t, col, o_r, stream=None) -> None:
@@ -442,13 +455,15 @@ class Buffers:
 
 def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
     """The whole step, fused where the library allows: the prologue writes Q'
-    in tile order and K' as K tiles, V is reordered into V tiles, blocks are
-    selected, and the attention writes O straight into raster order.
-    Returns the raster output tensor ``buf.o``."""
-    sva_qk_norm_rope_tiled(plan, q, k, wq, wk, buf.q_r, buf.k_t, stream)
+    in tile order, K' as K tiles and the block means, V is reordered into V
+    tiles, blocks are ranked from those means, and the attention writes O
+    straight into raster order.  Returns the raster output tensor ``buf.o``."""
+    sparse = not plan.info.dense
+    sva_qk_norm_rope_tiled(plan, q, k, wq, wk, buf.q_r, buf.k_t,
+                           buf.ws if sparse else None, stream)
     sva_reorder(plan, v, buf.v_t, SVA_FORWARD_VT, stream)
-    if not plan.info.dense:
-        sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
+    if sparse:
+        sva_select_blocks(plan, None, None, buf.ws, buf.col, stream)
     if plan.compensated:
         sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
     sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o,

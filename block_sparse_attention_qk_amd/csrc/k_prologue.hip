@@ -48,6 +48,7 @@ struct ProArgs {
     const uint16_t* in[2];
     uint16_t* out[2];
     const float* w[2];
+    double* mean[2];   // tiled kernel: block means to write, or NULL
 };
 
 template <int D>
@@ -166,57 +167,52 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(ProArgs a) {
 }
 
 // The prologue written straight into the attention layouts.  A workgroup
-// owns one 32-position group of the tile order (one K-tile group) for HG
-// consecutive heads of one batch; position pos holds raster token inv[pos]
-// (or padding).  Row R of the workgroup is (position R / HG, head R % HG),
-// so the rows a wave loads together are neighbouring heads of one token:
-// HG · d · 2 contiguous bytes of [B, N, H, d] instead of scattered d · 2
-// byte pieces.  Rows are loaded and computed exactly as in the raster kernel
-// (d/8 lanes per row, all of a thread's rows loaded before any is used;
-// HG divides the rows per pass, so a thread keeps one head), then
-//  Q' (KT = false): written as tile-order rows, 32 consecutive per head;
+// owns PW = 128 consecutive tile positions of one (b, h); position pos holds
+// raster token inv[pos] (or padding).  Rows are loaded and computed exactly
+// as in the raster kernel (d/8 lanes per row), with the token indices, the
+// rows and the cos/sin values each loaded as one branch-free batch (clamped
+// addresses, values discarded afterwards where a row does not exist), so a
+// thread's loads are in flight together.  Then
+//  Q' (KT = false): written as tile-order rows, contiguous per workgroup;
 //  K' (KT = true): staged in LDS (row stride padded by 16 bytes so the
 //     column reads below are free of bank conflicts) and written as K tiles:
-//     wave g owns heads g, g + 4, ..; lane 32·hf + j reads chunk 2s + hf of
+//     wave g owns the 32-token group g, lane 32·hf + j reads chunk 2s + hf of
 //     token j, so every step s writes one contiguous 1 KB span.
 // Padding positions (no raster token) are written as zeros.
-constexpr int kTileHeads = 4;   // HG
-
+//
+// With mean != NULL the workgroup also pools what it wrote, for the block
+// selection: float64 sums over each run of block/nsub positions (padding
+// rows are zeros and add nothing), divided by the run's valid count, stored
+// as the selection's q means [B,H,nB,nsub,d] or transposed k means
+// [B,H,d,nB·nsub].  Sums of at most 128 bf16 values are exact in float64 for
+// the data this sees, so the means equal those of a separate pooling pass.
 template <int D, bool KT>
 __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
-    constexpr int HG = kTileHeads;
     constexpr int LPR = D / 8;                 // 16-byte chunks (lanes) per row
     constexpr int DS = D / 16;                 // K-tile steps (chunk pairs)
+    constexpr int PW = 128;                    // positions per workgroup
     constexpr int RPP = kThreads / LPR;        // rows per pass
-    constexpr int NP = 32 * HG / RPP;          // rows per thread
+    constexpr int NP = PW / RPP;               // rows per thread
     constexpr int LS = LPR + 1;                // LDS row stride in chunks
-    static_assert(RPP % HG == 0, "a thread must keep one head");
-    __shared__ u32x4 stage[KT ? 32 * HG * LS : 1];
+    __shared__ u32x4 stage[PW * LS];
     const int tensor = KT ? 1 : 0;
     const DevPlan& p = a.p;
     const u32x4* in = reinterpret_cast<const u32x4*>(a.in[tensor]);
     u32x4* out = reinterpret_cast<u32x4*>(a.out[tensor]);
     const float* __restrict__ w = a.w[tensor];
-    const int ngroups = (int)(p.Np / 32);      // Np is a multiple of 32
-    const int nhg = (p.H + HG - 1) / HG;
-    const int64_t b = blockIdx.x / ((int64_t)ngroups * nhg);
-    const int rest = (int)(blockIdx.x - b * ((int64_t)ngroups * nhg));
-    const int grp = rest / nhg;
-    const int h0 = (rest - grp * nhg) * HG;
-    const int pos0 = grp * 32;
+    double* __restrict__ mean = a.mean[tensor];
+    const int per_head = (int)((p.Np + PW - 1) / PW);
+    const int64_t bh = blockIdx.x / per_head;
+    const int pos0 = (int)(blockIdx.x - bh * per_head) * PW;
+    const int64_t b = bh / p.H;
+    const int h = (int)(bh - b * p.H);
     const int sub = threadIdx.x % LPR;
     const int r0 = threadIdx.x / LPR;
-    const int h = h0 + r0 % HG;               // this thread's head
-    const bool hok = h < p.H;
     const uint32_t hw = (uint32_t)(p.Hh * p.W);
 
-    // Loads in three branch-free batches (token index, row, cos/sin), each
-    // address clamped to a valid one and the value discarded afterwards
-    // where the row does not exist, so that a batch is in flight at once.
-    const int hc = hok ? h : 0;
     float wv[8];   // issued first: the first row needs them
     if (w) {
-        const float4* wp = reinterpret_cast<const float4*>(w + hc * D + sub * 8);
+        const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
         const float4 w0 = wp[0], w1 = wp[1];
         wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
         wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
@@ -227,14 +223,15 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
     int nr[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        const int n = p.inv[pos0 + (r0 + i * RPP) / HG];   // Np is a multiple of 32
-        nr[i] = hok ? n : -2;                 // -2: no such head, -1: padding
+        const int pos = pos0 + r0 + i * RPP;
+        const int n = p.inv[pos < p.Np ? pos : p.Np - 1];
+        nr[i] = pos < p.Np ? n : -2;          // -2: past the end, -1: padding
     }
     u32x4 x[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int n = nr[i] >= 0 ? nr[i] : 0;
-        x[i] = in[((b * p.N + n) * p.H + hc) * LPR + sub];
+        x[i] = in[((b * p.N + n) * p.H + h) * LPR + sub];
     }
     // this lane's channel pairs: RoPE section (-1: none), offset in its
     // table and the section's width
@@ -256,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
             pi -= half;
         }
     }
-    // every row's cos/sin (the table always holds entry 0, the identity
+    // every row's cos/sin (the table always holds entry 0; the identity
     // rotation is substituted where a pair is not rotated)
     float2 cs[NP][4];
 #pragma unroll
@@ -289,7 +286,6 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int r = r0 + i * RPP;
-        const int n = nr[i];
         const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
         float v[8];
 #pragma unroll
@@ -303,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
 #pragma unroll
         for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
         u32x4 res = u32x4{0u, 0u, 0u, 0u};
-        if (n >= 0) {
+        if (nr[i] >= 0) {
             const float rs = rms_scale(ss, inv_d, p.eps);
             uint32_t ob[4];
 #pragma unroll
@@ -314,23 +310,65 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
             }
             res = u32x4{ob[0], ob[1], ob[2], ob[3]};
         }
-        if constexpr (KT) {
-            stage[r * LS + sub] = res;
-        } else {
-            if (hok) out[(((b * p.H + h) * p.Np) + pos0 + r / HG) * LPR + sub] = res;
+        if (KT || mean) stage[r * LS + sub] = res;
+        if (!KT && nr[i] != -2) out[(bh * p.Np + pos0 + r) * LPR + sub] = res;
+    }
+    if (!KT && !mean) return;
+    __syncthreads();
+    if constexpr (KT) {
+        const int g = threadIdx.x >> 6;        // 32-token group of this wave
+        const int lane = threadIdx.x & 63;
+        const int j = lane & 31, hf = lane >> 5;
+        const int gpos = pos0 + g * 32;        // Np is a multiple of 32
+        if (gpos < p.Np) {
+            const int kb = gpos / p.block, t = gpos - kb * p.block;
+            u32x4* dst = out + ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (DS * 64) + lane;
+#pragma unroll
+            for (int s2 = 0; s2 < DS; ++s2) dst[s2 * 64] = stage[(g * 32 + j) * LS + 2 * s2 + hf];
         }
     }
-    if constexpr (!KT) return;
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int j = lane & 31, hf = lane >> 5;
-    const int kb = pos0 / p.block, t = pos0 - kb * p.block;
-    for (int hl = threadIdx.x >> 6; hl < HG; hl += kThreads / 64) {
-        if (h0 + hl >= p.H) break;
-        const int64_t bh = b * p.H + h0 + hl;
-        u32x4* dst = out + ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (DS * 64) + lane;
+    if (!mean) return;
+
+    // Pooling.  Thread (slice sl, chunk c) sums 8-channel chunk c over the
+    // slice's SR rows; a run (block/nsub >= 16 rows) is a whole number of
+    // slices.  The slice sums go through LDS (over the staged rows, once
+    // every wave has read them), then one thread per (run, channel) adds
+    // its run's slices.
+    constexpr int NSL = kThreads / LPR;        // slices
+    constexpr int SR = PW / NSL;               // rows per slice (8 or 4)
+    const int sl = threadIdx.x / LPR, c = threadIdx.x % LPR;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int s2 = 0; s2 < DS; ++s2) dst[s2 * 64] = stage[(j * HG + hl) * LS + 2 * s2 + hf];
+    for (int rr = 0; rr < SR; ++rr) {
+        const u32x4 vv = stage[(sl * SR + rr) * LS + c];
+        const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)bf16lo(u[e]);
+            acc[2 * e + 1] += (double)bf16hi(u[e]);
+        }
+    }
+    __syncthreads();
+    double* part = reinterpret_cast<double*>(stage);   // [NSL][D]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[sl * D + c * 8 + e] = acc[e];
+    __syncthreads();
+    const int RL = p.block / p.nsub;           // rows per run
+    const int spr = RL / SR;                   // slices per run
+    for (int it = threadIdx.x; it < (PW / RL) * D; it += kThreads) {
+        const int run = it / D, ch = it - run * D;
+        const int rpos = pos0 + run * RL;
+        if (rpos >= p.Np) break;
+        double sum = 0.0;
+        for (int k2 = 0; k2 < spr; ++k2) sum += part[(run * spr + k2) * D + ch];
+        const int kb = rpos / p.block;
+        const int rib = (rpos - kb * p.block) / RL;   // run within the block
+        const int valid = min(max(p.blk_valid[kb] - rib * RL, 0), RL);
+        const double m = valid > 0 ? sum / (double)valid : 0.0;
+        if constexpr (KT)
+            mean[(bh * D + ch) * ((int64_t)p.nB * p.nsub) + (int64_t)kb * p.nsub + rib] = m;
+        else
+            mean[((bh * p.nB + kb) * p.nsub + rib) * D + ch] = m;
     }
 }
 
@@ -338,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
 
 hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
                            const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
-                           bool tiled, hipStream_t s) {
+                           bool tiled, double* means, hipStream_t s) {
     ProArgs a;
     a.p = p;
     a.in[0] = q;
@@ -347,13 +385,10 @@ hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* 
     a.out[1] = ko;
     a.w[0] = wq;
     a.w[1] = wk;
-    const int64_t rows = (int64_t)p.B * p.N * p.H;
-    const int lpr = p.d / 8;
-    const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
-    const int64_t blocks = (rows + per_block - 1) / per_block;
+    a.mean[0] = means;
+    a.mean[1] = means ? means + (int64_t)p.B * p.H * p.nB * p.nsub * p.d : nullptr;
     if (tiled) {
-        const int64_t nhg = (p.H + kTileHeads - 1) / kTileHeads;
-        dim3 gt((unsigned)((int64_t)p.B * (p.Np / 32) * nhg));
+        dim3 gt((unsigned)((int64_t)p.B * p.H * ((p.Np + 127) / 128)));
         if (p.d == 128) {
             hipLaunchKernelGGL((prologue_tiled_kernel<128, false>), gt, dim3(kThreads), 0, s, a);
             hipLaunchKernelGGL((prologue_tiled_kernel<128, true>), gt, dim3(kThreads), 0, s, a);
@@ -363,6 +398,10 @@ hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* 
         }
         return hipGetLastError();
     }
+    const int64_t rows = (int64_t)p.B * p.N * p.H;
+    const int lpr = p.d / 8;
+    const int64_t per_block = (int64_t)(kThreads / lpr) * kRows;
+    const int64_t blocks = (rows + per_block - 1) / per_block;
     dim3 grid((unsigned)blocks, 2);
     if (p.d == 128)
         hipLaunchKernelGGL(prologue_kernel<128>, grid, dim3(kThreads), 0, s, a);

@@ -353,7 +353,7 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     const int64_t BH = (int64_t)p.B * p.H;
     double* qmean = ws;                                  // [B,H,nB,nsub,d]
     double* kmeanT = ws + BH * p.nB * p.nsub * p.d;      // [B,H,d,nB·nsub]
-    {
+    if (qr && kt) {
         dim3 grid((unsigned)(BH * p.nB), (unsigned)p.nsub);
         const u32x4* q4 = reinterpret_cast<const u32x4*>(qr);
         const u32x4* k4 = reinterpret_cast<const u32x4*>(kt);

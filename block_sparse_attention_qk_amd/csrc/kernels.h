@@ -55,16 +55,18 @@ struct DevPlan {
 };
 
 // tiled: qo = Q' in tile order [B,H,Np,d], ko = K' tiles (padding zeroed);
-// otherwise both raster [B,N,H,d]
+// otherwise both raster [B,N,H,d].  means (tiled only, may be NULL): the
+// selection's block means, laid out as launch_select's workspace
 hipError_t launch_prologue(const DevPlan& p, const uint16_t* q, const uint16_t* k,
                            const float* wq, const float* wk, uint16_t* qo, uint16_t* ko,
-                           bool tiled, hipStream_t s);
+                           bool tiled, double* means, hipStream_t s);
 
 hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, int direction,
                           hipStream_t s);
 
-// qr: Q' in tile order; kt: K' as K tiles.
-// ws: [B,H,nB,d] q means followed by [B,H,d,nB] k means (float64)
+// qr: Q' in tile order; kt: K' as K tiles; both NULL: ws already holds the
+// means (written by the tiled prologue), only the ranking runs.
+// ws: [B,H,nB,nsub,d] q means followed by [B,H,d,nB·nsub] k means (float64)
 hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* kt, double* ws,
                          int32_t* col, hipStream_t s);
 

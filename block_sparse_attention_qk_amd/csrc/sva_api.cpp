@@ -199,26 +199,34 @@ int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k, const float* w
     hipError_t e = sva::launch_prologue(plan->dev, static_cast<const uint16_t*>(q),
                                         static_cast<const uint16_t*>(k), wq, wk,
                                         static_cast<uint16_t*>(q_out),
-                                        static_cast<uint16_t*>(k_out), false,
+                                        static_cast<uint16_t*>(k_out), false, nullptr,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "qk_norm_rope launch");
     return SVA_OK;
 }
 
 int sva_qk_norm_rope_tiled(sva_plan plan, const void* q, const void* k, const float* wq,
-                           const float* wk, void* q_r, void* k_t, void* stream) {
+                           const float* wk, void* q_r, void* k_t, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
     if (!q || !k || !q_r || !k_t)
         return set_err(SVA_ERR_INVALID_ARG, "q, k, q_r and k_t must be non-NULL");
     if (!sva::aligned16(q) || !sva::aligned16(k) || !sva::aligned16(q_r) ||
-        !sva::aligned16(k_t) || !sva::aligned16(wq) || !sva::aligned16(wk))
+        !sva::aligned16(k_t) || !sva::aligned16(wq) || !sva::aligned16(wk) ||
+        !sva::aligned16(workspace))
         return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     if (q_r == q || q_r == k || k_t == q || k_t == k)
         return set_err(SVA_ERR_INVALID_ARG, "outputs must not alias the inputs");
+    double* means = nullptr;
+    if (workspace && !plan->host.info.dense) {
+        if (workspace_bytes < plan->host.info.select_workspace_bytes)
+            return set_err(SVA_ERR_WORKSPACE, "workspace smaller than select_workspace_bytes");
+        means = static_cast<double*>(workspace);
+    }
     hipError_t e = sva::launch_prologue(plan->dev, static_cast<const uint16_t*>(q),
                                         static_cast<const uint16_t*>(k), wq, wk,
                                         static_cast<uint16_t*>(q_r),
-                                        static_cast<uint16_t*>(k_t), true,
+                                        static_cast<uint16_t*>(k_t), true, means,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "qk_norm_rope_tiled launch");
     return SVA_OK;
@@ -244,8 +252,11 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t, void* wor
                       size_t workspace_bytes, int32_t* col, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
     if (plan->host.info.dense) return SVA_OK;
-    if (!q_r || !k_t || !col || !workspace)
-        return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, workspace and col must be non-NULL");
+    if (!col || !workspace)
+        return set_err(SVA_ERR_INVALID_ARG, "workspace and col must be non-NULL");
+    if ((q_r == nullptr) != (k_t == nullptr))
+        return set_err(SVA_ERR_INVALID_ARG,
+                       "q_r and k_t must both be given, or both be NULL (means in the workspace)");
     if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(workspace) ||
         ((uintptr_t)col & 3u))
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");

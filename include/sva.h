@@ -201,10 +201,16 @@ int sva_qk_norm_rope(sva_plan plan, const void* q, const void* k,
  * reads (the reorders of Q' and K' fused away): q_r = Q' in tile order
  * [B, H, Np, d], k_t = K' as K tiles (the layouts of SVA_FORWARD and
  * SVA_FORWARD_KT), padding rows zero.  Bit-identical to sva_qk_norm_rope
- * followed by those reorders.  The outputs must not overlap the inputs. */
+ * followed by those reorders.  The outputs must not overlap the inputs.
+ * workspace (optional, device, workspace_bytes >= info.select_workspace_bytes):
+ * when given for a sparse plan, the kernel also pools what it writes into
+ * the block means that sva_select_blocks ranks ("lightweight pooling" of
+ * the SubBlock section, fused into the producer), so the selection need
+ * not read Q' and K' again: call sva_select_blocks with q_r = k_t = NULL
+ * and the same workspace.  Ignored for a dense plan; NULL skips it. */
 int sva_qk_norm_rope_tiled(sva_plan plan, const void* q, const void* k,
                            const float* wq, const float* wk, void* q_r, void* k_t,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token permutation between raster and 3D-tile order (see direction
  * macros).  Forward writes zeros into the padding rows; the inverse drops
@@ -213,6 +219,9 @@ int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* s
 
 /* Block selection.  q_r: tile order [B, H, Np, d] (SVA_FORWARD of Q');
  * k_t: K tiles (SVA_FORWARD_KT of K', the same buffer sva_attention reads).
+ * q_r and k_t both NULL: the workspace already holds the block means,
+ * written by sva_qk_norm_rope_tiled with this workspace (only the ranking
+ * runs); one of them NULL is an argument error.
  * For every (b, h, query block qb): score(kb) by the plan's scorer (means
  * over valid tokens, float64); keep the forced blocks and then the
  * best-scored blocks (score descending, lower block index first on

@@ -115,6 +115,9 @@ def test_null_arguments_rejected_on_host():
     assert L.sva_reorder(None, None, None, 0, None) == S.SVA_ERR_INVALID_ARG
     assert L.sva_select_blocks(None, None, None, None, 0, None, None) == S.SVA_ERR_INVALID_ARG
     assert L.sva_attention(None, None, None, None, None, None, None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_qk_norm_rope_tiled(None, None, None, None, None, None, None, None, 0,
+                                    None) == S.SVA_ERR_INVALID_ARG
+    assert L.sva_block_means(None, None, None, None, None, None) == S.SVA_ERR_INVALID_ARG
     assert L.sva_destroy(None) == S.SVA_OK
     assert L.sva_plan_create_ex(None, None) == S.SVA_ERR_INVALID_ARG
 

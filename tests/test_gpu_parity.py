@@ -260,6 +260,31 @@ def test_tiled_prologue_is_prologue_plus_reorders(name):
     assert np.array_equal(host(kt_t), host(run.buf.k_t))
 
 
+@pytest.mark.parametrize("name", [n for n in SMALL if not SMALL[n].flags & I.DENSE
+                                  and SMALL[n].sparsity > 0])
+def test_fused_pooling_equals_select_pooling(name):
+    """The block means the tiled prologue writes into the select workspace
+    equal, bit for bit, those sva_select_blocks pools from Q' and K' (sums of
+    bf16 values are exact in float64 here), and ranking them gives the same
+    block lists."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    b = run.buf
+    ws2 = torch.empty_like(b.ws)
+    col2 = torch.empty_like(b.col)
+    b.ws.fill_(0x7F)   # stale bytes would show
+    S.sva_qk_norm_rope_tiled(run.plan, run.q, run.k, run.wq, run.wk, b.q_r, b.k_t, b.ws)
+    S.sva_select_blocks(run.plan, None, None, b.ws, b.col)
+    S.sva_select_blocks(run.plan, b.q_r, b.k_t, ws2, col2)
+    torch.cuda.synchronize()
+    info = run.plan.info
+    n_means = 2 * wl.B * wl.H * int(info.nB) * int(info.subblocks) * wl.d
+    m1 = b.ws.view(torch.float64)[:n_means].cpu().numpy()
+    m2 = ws2.view(torch.float64)[:n_means].cpu().numpy()
+    assert np.array_equal(m1.view(np.uint64), m2.view(np.uint64))
+    assert torch.equal(b.col, col2)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_raster_output_is_inverse_reorder(name):
     """sva_attention_ex with the raster layout equals the tile-order output
@@ -365,6 +390,14 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(S.SvaError) as e:
         S.sva_select_blocks(plan, buf.q_r, buf.k_t, small_ws, buf.col)
     assert e.value.status == S.SVA_ERR_WORKSPACE
+    with pytest.raises(S.SvaError) as e:
+        S.sva_select_blocks(plan, buf.q_r, None, buf.ws, buf.col)
+    assert e.value.status == S.SVA_ERR_INVALID_ARG
+    if not plan.info.dense:
+        dq = torch.zeros(plan.raster_shape, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(S.SvaError) as e:
+            S.sva_qk_norm_rope_tiled(plan, dq, dq, None, None, buf.q_r, buf.k_t, small_ws)
+        assert e.value.status == S.SVA_ERR_WORKSPACE
 
 
 # ------------------------------------------------------------------ full-size workloads
