@@ -129,8 +129,13 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
         const u32x4 v = n[j] >= 0 ? x[j] : u32x4{0u, 0u, 0u, 0u};
         m[j][0] = v.x; m[j][1] = v.y; m[j][2] = v.z; m[j][3] = v.w;
     }
-    // 32-key group kg/4, chunk kg%4: d rows of 8 keys
-    u32x4* dst = out + (((bh * p.nB + kb) * (BLK / 32) + (kg >> 2)) * 4 + (kg & 3)) * D + dc * 8;
+    // 32-key group kg/4, chunk kg%4: d rows of 8 keys, i.e. output chunks
+    // kg·D + dc·8 + e of the block's tile.  They go through LDS (one padding
+    // chunk after every 8, so the 16 lanes of a row group hit distinct
+    // banks) and leave as contiguous 1 KB wave stores.
+    constexpr int NTH = (D / 8) * (BLK / 8);
+    constexpr int TCH = BLK * D / 8;          // 16-byte chunks per block tile
+    __shared__ u32x4 tile[TCH + TCH / 8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         uint32_t o[4];
@@ -140,7 +145,15 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
             o[w] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
                            : ((lo & 0xffffu) | (hi << 16));
         }
-        dst[e] = u32x4{o[0], o[1], o[2], o[3]};
+        const int q = kg * D + dc * 8 + e;
+        tile[q + (q >> 3)] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    __syncthreads();
+    u32x4* dst = out + (bh * p.nB + kb) * (int64_t)TCH;
+#pragma unroll
+    for (int i = 0; i < TCH / NTH; ++i) {
+        const int q = threadIdx.x + i * NTH;
+        dst[q] = tile[q + (q >> 3)];
     }
 }
 
