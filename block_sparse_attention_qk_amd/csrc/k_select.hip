@@ -21,9 +21,10 @@
 //         means are stored [B,H,nB,d], k means transposed [B,H,d,nB] so the
 //         score loop reads them coalesced.
 //  topk   one workgroup per (b, h, R <= 8 query blocks): float64 scores of
-//         the R rows against every key block into LDS (each thread walks one
-//         key block's transposed mean with 16 loads in flight, the query
-//         means broadcast from LDS), then one wave per row
+//         the R rows against every key block into LDS (each thread computes
+//         two rows against four consecutive key runs, so one LDS read of the
+//         query means feeds four fma; reading them once per fma would make
+//         the loop bound by LDS bandwidth), then one wave per row
 //         finds the r-th largest eligible score by a bitwise search on
 //         order-preserving 64-bit keys (ballot + popcount, no sorting),
 //         takes equal scores lowest index first, and writes the kept
@@ -149,23 +150,24 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
     return v;
 }
 
-// log of the valid count of run a of block b (-inf for an empty run)
-__device__ __forceinline__ double log_count(const DevPlan& p, int b, int a) {
+// valid tokens of run a of block b
+__device__ __forceinline__ int run_count(const DevPlan& p, int b, int a) {
     const int sb = p.block / p.nsub;
-    const int c = min(max(p.blk_valid[b] - a * sb, 0), sb);
-    return c > 0 ? log((double)c) : -INFINITY;
+    return min(max(p.blk_valid[b] - a * sb, 0), sb);
 }
 
 template <int D, int NSLOT, int NSUB>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const double* qmean,
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
-    constexpr int RT = 8;              // rows computed per pass over the key means
-    constexpr int DB = 16;             // key-mean loads in flight per thread
-    constexpr int QW = RT * NSUB;      // query runs held per pass
+    constexpr int RT = 8;              // rows per workgroup pass (R <= RT)
+    constexpr int DB = 8;              // channels of key means loaded per batch
+    constexpr int QW = RT * NSUB;      // query runs held in LDS
+    constexpr int QT = 2 * NSUB;       // query runs per thread (two rows)
     extern __shared__ double smem[];
     double* qs = smem;                 // [D][QW], rows past nrows zero
     double* sc = smem + QW * D;        // [R][nB]
+    double* lgt = sc + R * p.nB;       // [block + 1]: log of a run's valid count
     const int nB = p.nB;
     const int groups = (nB + R - 1) / R;
     const int g = blockIdx.x % groups;
@@ -177,22 +179,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
         const int dd = i / QW, ra = i % QW;
         qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
     }
+    if (!(NSUB == 1 && p.scorer == 0))
+        for (int c = threadIdx.x; c <= p.block; c += kTopkThreads)
+            lgt[c] = c > 0 ? log((double)c) : -INFINITY;
     __syncthreads();
 
     const double* kt = kmeanT + bh * D * (int64_t)nB * NSUB;
     if (NSUB == 1 && p.scorer == 0) {
-        // mean scorer: thread per key block, all RT rows at once; each score
-        // is the sequential fma chain over the channels
+        // Mean scorer: thread per key block, all RT rows at once (its key
+        // means are one 512-byte wave load per channel, the query means a
+        // broadcast LDS read); each score is the sequential fma chain over
+        // the channels.
+        constexpr int DBM = 16;
         for (int kb = threadIdx.x; kb < nB; kb += kTopkThreads) {
             double acc[RT];
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc[r] = 0.0;
-            for (int d0 = 0; d0 < D; d0 += DB) {
-                double kv[DB];
+            for (int d0 = 0; d0 < D; d0 += DBM) {
+                double kv[DBM];
 #pragma unroll
-                for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nB + kb];
+                for (int i = 0; i < DBM; ++i) kv[i] = kt[(int64_t)(d0 + i) * nB + kb];
 #pragma unroll
-                for (int i = 0; i < DB; ++i) {
+                for (int i = 0; i < DBM; ++i) {
                     const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * RT);
 #pragma unroll
                     for (int r2 = 0; r2 < RT / 2; ++r2) {
@@ -207,65 +215,82 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                 if (r < nrows) sc[r * nB + kb] = acc[r];
         }
     } else {
-        // SubBlock scorer: thread per key run (kb, b), the NSUB runs of a key
-        // block in adjacent lanes.  Dot products with every query run of the
-        // RT rows, then per row the log-sum-exp over query runs (in the
-        // thread) and key runs (across the NSUB lanes).
-        const double inv_sqrt_d = 1.0 / sqrt((double)D);
+        // SubBlock scorer, as a register-blocked product: thread (kg, rp) =
+        // (t / 4, t % 4) holds the QT query runs of rows 2rp, 2rp + 1 against
+        // the 4 consecutive key runs ks0 .. ks0 + 3 (run ks = kb·NSUB + b of the
+        // transposed key means).  Per channel: QT query values from LDS (one
+        // address per lane quad), 4 key values, 4·QT fma, each a sequential
+        // chain over the channels; one LDS read feeds four fma (one per fma
+        // would make the loop bound by LDS bandwidth).  NSUB divides 4, so a
+        // thread holds every key run of its key blocks and finishes the estimate
+        //   log sum_a sum_b c_a c_b exp(qbar_a · kbar_b / sqrt(d))
+        // itself.
         const int nks = nB * NSUB;
-        const int iters = (nks + kTopkThreads - 1) / kTopkThreads;
-        for (int it = 0; it < iters; ++it) {
-            const int ks = it * kTopkThreads + threadIdx.x;
-            const bool act = ks < nks;
-            const int kcol = act ? ks : nks - 1;
-            double acc[QW];
+        const int rp = threadIdx.x & 3, kg = threadIdx.x >> 2;
+        const double inv_sqrt_d = 1.0 / sqrt((double)D);
+        double lq[2][NSUB];   // log valid counts of this thread's query runs
 #pragma unroll
-            for (int r = 0; r < QW; ++r) acc[r] = 0.0;
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int aa = 0; aa < NSUB; ++aa)
+                lq[rr][aa] = lgt[run_count(p, qb0 + min(2 * rp + rr, nrows - 1), aa)];
+        for (int ks0 = kg * 4; ks0 < nks; ks0 += kTopkThreads) {
+            double acc[QT][4];
+#pragma unroll
+            for (int a2 = 0; a2 < QT; ++a2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[a2][j] = 0.0;
+            int kcol[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kcol[j] = min(ks0 + j, nks - 1);
             for (int d0 = 0; d0 < D; d0 += DB) {
-                double kv[DB];
+                double kv[DB][4];
 #pragma unroll
-                for (int i = 0; i < DB; ++i) kv[i] = kt[(int64_t)(d0 + i) * nks + kcol];
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kv[i][j] = kt[(int64_t)(d0 + i) * nks + kcol[j]];
 #pragma unroll
                 for (int i = 0; i < DB; ++i) {
-                    const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * QW);
+                    const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * QW + rp * QT);
 #pragma unroll
-                    for (int r2 = 0; r2 < QW / 2; ++r2) {
-                        const double2 qq = q2[r2];
-                        acc[2 * r2] = fma(qq.x, kv[i], acc[2 * r2]);
-                        acc[2 * r2 + 1] = fma(qq.y, kv[i], acc[2 * r2 + 1]);
+                    for (int a2 = 0; a2 < QT / 2; ++a2) {
+                        const double2 qq = q2[a2];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            acc[2 * a2][j] = fma(qq.x, kv[i][j], acc[2 * a2][j]);
+                            acc[2 * a2 + 1][j] = fma(qq.y, kv[i][j], acc[2 * a2 + 1][j]);
+                        }
                     }
                 }
             }
-            const int kb = kcol / NSUB, b = kcol % NSUB;
-            const double lk = log_count(p, kb, b);
 #pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                const int qb = qb0 + min(r, nrows - 1);
-                double m = -INFINITY;
-                double x[NSUB];
+            for (int kk = 0; kk < 4 / NSUB; ++kk) {
+                const int kb = ks0 / NSUB + kk;
+                double lk[NSUB];
 #pragma unroll
-                for (int a = 0; a < NSUB; ++a) {
-                    x[a] = acc[r * NSUB + a] * inv_sqrt_d + log_count(p, qb, a) + lk;
-                    m = fmax(m, x[a]);
-                }
-                double sum = 0.0;
-                if (m > -INFINITY) {
+                for (int bb = 0; bb < NSUB; ++bb) lk[bb] = lgt[run_count(p, min(kb, nB - 1), bb)];
 #pragma unroll
-                    for (int a = 0; a < NSUB; ++a) sum += exp(x[a] - m);
-                }
-                // combine the NSUB key runs of this key block (adjacent lanes)
+                for (int rr = 0; rr < 2; ++rr) {
+                    double x[NSUB][NSUB];
+                    double m = -INFINITY;
 #pragma unroll
-                for (int off = 1; off < NSUB; off <<= 1) {
-                    const double mo = __shfl_xor(m, off, 64);
-                    const double so = __shfl_xor(sum, off, 64);
-                    const double mn = fmax(m, mo);
-                    if (mn > -INFINITY) {
-                        sum = (m > -INFINITY ? sum * exp(m - mn) : 0.0) +
-                              (mo > -INFINITY ? so * exp(mo - mn) : 0.0);
-                        m = mn;
+                    for (int aa = 0; aa < NSUB; ++aa)
+#pragma unroll
+                        for (int bb = 0; bb < NSUB; ++bb) {
+                            x[aa][bb] = acc[rr * NSUB + aa][kk * NSUB + bb] * inv_sqrt_d +
+                                        lq[rr][aa] + lk[bb];
+                            m = fmax(m, x[aa][bb]);
+                        }
+                    double sum = 0.0;
+                    if (m > -INFINITY) {
+#pragma unroll
+                        for (int aa = 0; aa < NSUB; ++aa)
+#pragma unroll
+                            for (int bb = 0; bb < NSUB; ++bb) sum += exp(x[aa][bb] - m);
                     }
+                    const int r = 2 * rp + rr;
+                    if (r < nrows && kb < nB) sc[r * nB + kb] = m + log(sum);
                 }
-                if (act && b == 0 && r < nrows) sc[r * nB + kb] = m + log(sum);
             }
         }
     }
@@ -380,7 +405,8 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
     const int groups = (p.nB + R - 1) / R;
     dim3 grid((unsigned)(BH * groups));
-    const size_t lds = (size_t)qbytes + (size_t)R * p.nB * sizeof(double);
+    const size_t lds = (size_t)qbytes + (size_t)R * p.nB * sizeof(double) +
+                       (size_t)(p.block + 1) * sizeof(double);
     const int nslot = (p.nB + 63) / 64;
 #define SVA_TOPK(DD, NS, NSB) \
     hipLaunchKernelGGL((topk_kernel<DD, NS, NSB>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
