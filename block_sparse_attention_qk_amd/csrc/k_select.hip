@@ -156,12 +156,12 @@ __device__ __forceinline__ int run_count(const DevPlan& p, int b, int a) {
     return min(max(p.blk_valid[b] - a * sb, 0), sb);
 }
 
-template <int D, int NSLOT, int NSUB>
+template <int D, int NSLOT, int NSUB, bool SUBBLOCK>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const double* qmean,
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
     constexpr int RT = 8;              // rows per workgroup pass (R <= RT)
-    constexpr int DB = 8;              // channels of key means loaded per batch
+    constexpr int DB = 4;              // channels of key means loaded per batch
     constexpr int QW = RT * NSUB;      // query runs held in LDS
     constexpr int QT = 2 * NSUB;       // query runs per thread (two rows)
     extern __shared__ double smem[];
@@ -179,13 +179,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
         const int dd = i / QW, ra = i % QW;
         qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
     }
-    if (!(NSUB == 1 && p.scorer == 0))
+    if (SUBBLOCK)
         for (int c = threadIdx.x; c <= p.block; c += kTopkThreads)
             lgt[c] = c > 0 ? log((double)c) : -INFINITY;
     __syncthreads();
 
     const double* kt = kmeanT + bh * D * (int64_t)nB * NSUB;
-    if (NSUB == 1 && p.scorer == 0) {
+    if constexpr (!SUBBLOCK) {
         // Mean scorer: thread per key block, all RT rows at once (its key
         // means are one 512-byte wave load per channel, the query means a
         // broadcast LDS read); each score is the sequential fma chain over
@@ -243,12 +243,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
             int kcol[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) kcol[j] = min(ks0 + j, nks - 1);
+            // key means in batches of DB channels, the next batch loaded
+            // while the current one is multiplied
+            double kn[DB][4];
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kn[i][j] = kt[(int64_t)i * nks + kcol[j]];
             for (int d0 = 0; d0 < D; d0 += DB) {
                 double kv[DB][4];
 #pragma unroll
                 for (int i = 0; i < DB; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) kv[i][j] = kt[(int64_t)(d0 + i) * nks + kcol[j]];
+                    for (int j = 0; j < 4; ++j) kv[i][j] = kn[i][j];
+                if (d0 + DB < D) {
+#pragma unroll
+                    for (int i = 0; i < DB; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            kn[i][j] = kt[(int64_t)(d0 + DB + i) * nks + kcol[j]];
+                }
 #pragma unroll
                 for (int i = 0; i < DB; ++i) {
                     const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * QW + rp * QT);
@@ -408,22 +422,24 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     const size_t lds = (size_t)qbytes + (size_t)R * p.nB * sizeof(double) +
                        (size_t)(p.block + 1) * sizeof(double);
     const int nslot = (p.nB + 63) / 64;
-#define SVA_TOPK(DD, NS, NSB) \
-    hipLaunchKernelGGL((topk_kernel<DD, NS, NSB>), grid, dim3(kTopkThreads), lds, s, p, qmean, kmeanT, R, col)
-#define SVA_TOPK_S(DD, NSB)                                                                  \
+#define SVA_TOPK(DD, NS, NSB, SBK)                                                           \
+    hipLaunchKernelGGL((topk_kernel<DD, NS, NSB, SBK>), grid, dim3(kTopkThreads), lds, s, p,  \
+                       qmean, kmeanT, R, col)
+#define SVA_TOPK_S(DD, NSB, SBK)                                                             \
     do {                                                                                     \
-        if (nslot <= 4) SVA_TOPK(DD, 4, NSB);                                                \
-        else if (nslot <= 8) SVA_TOPK(DD, 8, NSB);                                           \
-        else if (nslot <= 12) SVA_TOPK(DD, 12, NSB);                                         \
-        else if (nslot <= 16) SVA_TOPK(DD, 16, NSB);                                         \
-        else if (nslot <= 32) SVA_TOPK(DD, 32, NSB);                                         \
-        else SVA_TOPK(DD, 64, NSB);                                                          \
+        if (nslot <= 4) SVA_TOPK(DD, 4, NSB, SBK);                                           \
+        else if (nslot <= 8) SVA_TOPK(DD, 8, NSB, SBK);                                      \
+        else if (nslot <= 12) SVA_TOPK(DD, 12, NSB, SBK);                                    \
+        else if (nslot <= 16) SVA_TOPK(DD, 16, NSB, SBK);                                    \
+        else if (nslot <= 32) SVA_TOPK(DD, 32, NSB, SBK);                                    \
+        else SVA_TOPK(DD, 64, NSB, SBK);                                                     \
     } while (0)
 #define SVA_TOPK_D(DD)                                                                       \
     do {                                                                                     \
-        if (p.nsub == 1) SVA_TOPK_S(DD, 1);                                                  \
-        else if (p.nsub == 2) SVA_TOPK_S(DD, 2);                                             \
-        else SVA_TOPK_S(DD, 4);                                                              \
+        if (p.scorer == 0) SVA_TOPK_S(DD, 1, false); /* mean scorer */                 \
+        else if (p.nsub == 1) SVA_TOPK_S(DD, 1, true);                                       \
+        else if (p.nsub == 2) SVA_TOPK_S(DD, 2, true);                                       \
+        else SVA_TOPK_S(DD, 4, true);                                                        \
     } while (0)
     if (p.d == 128) SVA_TOPK_D(128);
     else SVA_TOPK_D(64);
