@@ -9,7 +9,9 @@
 // attention ("SVA_DENSE", the dense warm-up steps of the same page).
 //
 // Work split: one workgroup per (b, h, qb), one wave per 32 query rows
-// (BLK/32 waves), two workgroups per CU.  A row's key blocks are consumed
+// (BLK/32 waves), two workgroups per CU.  A dense plan, whose rows all walk
+// every block, gives a workgroup two query blocks, so one copy of each K/V
+// stage feeds twice the waves.  A row's key blocks are consumed
 // in stages of 32 keys.  Both operand streams come in MFMA-ready tile
 // layouts written by the reorder kernels (K tiles, V tiles), in which one
 // stage of K and one stage of V are each a contiguous span of 32·d bf16.
@@ -135,12 +137,16 @@ constexpr int attn_stage_buffers(int d, int blk) {
 // spreads into AGPRs (238 registers) and runs 3 % slower.
 constexpr int attn_min_waves(int, int) { return 2; }
 
-template <int D, int BLK, bool DENSE, bool COMP>
-__global__ __launch_bounds__(BLK * 2)
+// QPW query blocks per workgroup: 1, or 2 for dense plans, whose rows all
+// walk the same list, so one copy of each K/V stage feeds twice the waves.
+template <int D, int BLK, bool DENSE, bool COMP, int QPW>
+__global__ __launch_bounds__(BLK * 2 * QPW)
 __attribute__((amdgpu_waves_per_eu(attn_min_waves(D, BLK), 2)))
 void attn_kernel(AttnArgs a) {
-    constexpr int NT = BLK * 2;          // threads (BLK/32 waves)
+    static_assert(QPW == 1 || DENSE, "only dense rows share one walk");
+    constexpr int NT = BLK * 2 * QPW;    // threads (QPW·BLK/32 waves)
     constexpr int NWV = NT / 64;
+    constexpr int WPB = BLK / 32;        // waves per query block
     constexpr int SK = 32;               // keys per stage (one 32-key MFMA tile)
     constexpr int SPB = BLK / SK;        // stages per block
     constexpr int KCH = D / 8;           // 16-byte chunks per Q row
@@ -162,13 +168,18 @@ void attn_kernel(AttnArgs a) {
                                          // then a bitmap of it (compensation)
 
     const DevPlan& p = a.p;
+    const int ngrp = (p.nB + QPW - 1) / QPW;
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int qb = (int)(wg % p.nB);
-    const int64_t bh = wg / p.nB;
+    const int qg = (int)(wg % ngrp);     // group of QPW query blocks
+    const int64_t bh = wg / ngrp;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
-    const int qrow = wave * 32 + j;      // query row within the block
+    // this wave's query block; past the last block (odd nB, QPW = 2) the
+    // wave computes on the last block's rows and stores nothing
+    const bool q_ok = qg * QPW + wave / WPB < p.nB;
+    const int qb = q_ok ? qg * QPW + wave / WPB : p.nB - 1;
+    const int qrow = (wave % WPB) * 32 + j;   // query row within the block
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
 
     // Q^T operand: lane (j, hf) holds channels 16s + 8hf .. +8 of row qrow
@@ -213,7 +224,7 @@ void attn_kernel(AttnArgs a) {
     // than walking every row from block 0 on the 75.6k-token workload).
     int rot = 0;
     {
-        const int kstart = qb & ~63;
+        const int kstart = (qg * QPW) & ~63;   // the same for every wave
         if (DENSE) {
             rot = kstart < len ? kstart : 0;
         } else {
@@ -458,6 +469,7 @@ void attn_kernel(AttnArgs a) {
     // epilogue: O = O^T / l.  Tile order: padding query rows are written as
     // zeros.  Raster order: row qrow goes to raster token inv[qb·BLK + qrow]
     // (the inverse reorder fused away); padding rows have none.
+    if (!q_ok) return;
     const float lt = lane_swap_sum(l);
     const bool row_ok = qrow < p.blk_valid[qb];
     const float inv = (row_ok && lt > 0.f) ? 1.f / lt : 0.f;
@@ -499,28 +511,32 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
     a.vm = reinterpret_cast<const u32x4_t*>(vm);
     a.o = reinterpret_cast<uint2*>(o);
     a.o_raster = o_raster ? 1 : 0;
-    dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
-    dim3 block(p.block * 2);
+    // dense plans: two query blocks per workgroup, except d = 64 with
+    // 128-token blocks, whose stage copy (256 chunks) cannot be split over
+    // eight waves
+    const int qpw = (p.dense && !(p.d == 64 && p.block == 128)) ? 2 : 1;
+    dim3 grid((unsigned)((int64_t)p.B * p.H * ((p.nB + qpw - 1) / qpw)));
+    dim3 block(p.block * 2 * qpw);
     const size_t lds = p.dense ? 0
                      : (size_t)(p.max_row_len + (km ? p.n_mean_groups : 0)) * sizeof(int32_t);
     auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a); };
     // dense plans have nothing to compensate; compensation is its own
     // instantiation so the plain kernels carry none of it
     if (p.dense) {
-        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, true, false>);
-        else if (p.d == 128) launch(attn_kernel<128, 64, true, false>);
-        else if (p.block == 128) launch(attn_kernel<64, 128, true, false>);
-        else launch(attn_kernel<64, 64, true, false>);
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, true, false, 2>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, true, false, 2>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, true, false, 1>);
+        else launch(attn_kernel<64, 64, true, false, 2>);
     } else if (!km) {
-        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, false>);
-        else if (p.d == 128) launch(attn_kernel<128, 64, false, false>);
-        else if (p.block == 128) launch(attn_kernel<64, 128, false, false>);
-        else launch(attn_kernel<64, 64, false, false>);
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, false, 1>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, false, false, 1>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, false, false, 1>);
+        else launch(attn_kernel<64, 64, false, false, 1>);
     } else {
-        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, true>);
-        else if (p.d == 128) launch(attn_kernel<128, 64, false, true>);
-        else if (p.block == 128) launch(attn_kernel<64, 128, false, true>);
-        else launch(attn_kernel<64, 64, false, true>);
+        if (p.d == 128 && p.block == 128) launch(attn_kernel<128, 128, false, true, 1>);
+        else if (p.d == 128) launch(attn_kernel<128, 64, false, true, 1>);
+        else if (p.block == 128) launch(attn_kernel<64, 128, false, true, 1>);
+        else launch(attn_kernel<64, 64, false, true, 1>);
     }
     return hipGetLastError();
 }

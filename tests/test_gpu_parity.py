@@ -59,6 +59,10 @@ SMALL = {
                         flags=I.COMPENSATE | I.KEEP_SAME_FRAME, n_extra=128, seed_base=10100),
     "comp64": I.custom("comp64", 2, 2, 3, 10, 14, 64, 64, 0.7, tile=(2, 4, 8),
                        flags=I.COMPENSATE, seed_base=10200),
+    # dense, d = 128 with 64-token blocks (two query blocks per workgroup),
+    # an odd number of blocks, extra tokens, B = 2
+    "dense_d128_b64": I.custom("dense_d128_b64", 2, 2, 3, 10, 14, 128, 64, 0.0, tile=(2, 4, 8),
+                               n_extra=128, seed_base=10300),
 }
 
 
