@@ -175,10 +175,15 @@ void attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
+    // First query block of the group.  Sparse plans start each head with
+    // the blocks of extra tokens: their rows keep every block and are the
+    // longest, so they must not be the last to begin.
+    const int nx = p.nB - p.nB_video;
+    const int qfirst = QPW == 1 ? (qg < nx ? p.nB_video + qg : qg - nx) : qg * QPW;
     // this wave's query block; past the last block (odd nB, QPW = 2) the
     // wave computes on the last block's rows and stores nothing
-    const bool q_ok = qg * QPW + wave / WPB < p.nB;
-    const int qb = q_ok ? qg * QPW + wave / WPB : p.nB - 1;
+    const bool q_ok = qfirst + wave / WPB < p.nB;
+    const int qb = q_ok ? qfirst + wave / WPB : p.nB - 1;
     const int qrow = (wave % WPB) * 32 + j;   // query row within the block
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
 
@@ -224,7 +229,7 @@ void attn_kernel(AttnArgs a) {
     // than walking every row from block 0 on the 75.6k-token workload).
     int rot = 0;
     {
-        const int kstart = (qg * QPW) & ~63;   // the same for every wave
+        const int kstart = qfirst & ~63;   // the same for every wave
         if (DENSE) {
             rot = kstart < len ? kstart : 0;
         } else {

@@ -124,7 +124,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kt_kernel(DevPlan p, const 
 }
 
 constexpr int kTopkThreads = 256;
-constexpr int kScoreLds = 65536;   // bytes of LDS for the q means and score rows
+// bytes of LDS for the q means and score rows: up to 8 rows per workgroup
+// (each row costs nB·8 bytes); large enough for 4 rows at the plan's
+// maximum of 4096 blocks, so a workgroup reads the key means for 4 rows at
+// once instead of one
+constexpr int kScoreLds = 147456;
 
 __device__ __forceinline__ uint64_t order_key(double s) {
     // canonical +0, then flip so unsigned order = numeric order

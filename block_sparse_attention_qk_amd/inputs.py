@@ -93,6 +93,14 @@ WORKLOADS = {
     "wan720p_subblock": Workload("wan720p_subblock", 1, 40, 21, 45, 80, 128, 128, 0.75,
                                  flags=KEEP_SAME_FRAME, tile=(2, 8, 8), temperature=True,
                                  seed_base=2000, scorer=1, budget_multiple=8),
+    # size limits: 4096 blocks per head (the plan's maximum; 262,144 tokens in
+    # 64-token blocks), and 1538 blocks (1536 video + 2 of extra tokens, whose
+    # rows and columns are always kept)
+    "max4096": Workload("max4096", 1, 2, 16, 128, 128, 64, 64, 0.9, tile=(4, 4, 4),
+                        seed_base=5000),
+    "blocks1538": Workload("blocks1538", 1, 1, 24, 64, 128, 128, 128, 0.85,
+                           flags=KEEP_SAME_FRAME, tile=(2, 8, 8), n_extra=256,
+                           seed_base=6000),
 }
 
 

@@ -407,7 +407,8 @@ def test_binding_rejects_bad_tensors():
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["wan480p_dense", "wan480p_sp75", "wan720p_sp75", "hunyuan720p_sp80",
-        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock", "hunyuan720p_comp"]
+        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock", "hunyuan720p_comp",
+        "max4096", "blocks1538"]
 _full_cache = {}
 
 
