@@ -263,6 +263,23 @@ void attn_kernel(AttnArgs a) {
             lds_dma16(vbase + off_ + e_, lds_addr(VB_ + e_));                        \
         }                                                                            \
     } while (0)
+    // the same two with the stage's block index given (KBI)
+#define SVA_DMA_KB(st, KBI, KB_, VB_)                                                \
+    do {                                                                             \
+        const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
+        const int kb_ = (KBI);                                                       \
+        const int64_t off_ = ((int64_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * CPS; \
+        _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
+            const int e_ = (i * NWV + wave_u) * 64;                                  \
+            lds_dma16(kbase + off_ + e_, lds_addr(KB_ + e_));                        \
+            lds_dma16(vbase + off_ + e_, lds_addr(VB_ + e_));                        \
+        }                                                                            \
+    } while (0)
+#define SVA_LIM_KB(st, KBI)                                                          \
+    ([&](int sl_, int kb_) {                                                         \
+        return (sl_ >= nstage || kb_ < 0) ? 0                                        \
+             : (kb_ == last_video ? min(last_valid - (sl_ % SPB) * SK, SK) : SK);    \
+    }(st, KBI))
     // S^T of stage st into SC from the K buffer KB_
 #define SVA_SCORE(KB_, SC)                                                           \
     do {                                                                             \
@@ -373,11 +390,27 @@ void attn_kernel(AttnArgs a) {
     }
     // unrolled by NBUF so every buffer index is a constant
     for (int st = 0; st < nstage; st += NBUF) {
+        // With NBUF == SPB the body's stages st .. st+SPB-1 are one list
+        // entry and the next SPB stages the next one (nstage is a multiple of
+        // SPB, so either all of them exist or all clamp to the last stage):
+        // two block-index lookups per body instead of two per stage.
+        int kbA = 0, kbB = 0;
+        if constexpr (NBUF == SPB) {
+            kbA = SVA_KB(st);
+            kbB = SVA_KB(st + SPB);
+        }
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
             if (u == 0 || st + u < nstage) {
-                SVA_DMA(st + u + NBUF - 1, sK[(u + NBUF - 1) % NBUF], sV[(u + NBUF - 1) % NBUF]);
-                const int lim = SVA_LIM(st + u + 1);
+                int lim;
+                if constexpr (NBUF == SPB) {
+                    SVA_DMA_KB(st + u + NBUF - 1, u == 0 ? kbA : kbB, sK[(u + NBUF - 1) % NBUF],
+                               sV[(u + NBUF - 1) % NBUF]);
+                    lim = SVA_LIM_KB(st + u + 1, u < NBUF - 1 ? kbA : kbB);
+                } else {
+                    SVA_DMA(st + u + NBUF - 1, sK[(u + NBUF - 1) % NBUF], sV[(u + NBUF - 1) % NBUF]);
+                    lim = SVA_LIM(st + u + 1);
+                }
                 // one straight-line region: the scheduler interleaves the
                 // matrix and vector halves
                 SVA_SCORE(sK[(u + 1) % NBUF], sn);
@@ -469,6 +502,8 @@ void attn_kernel(AttnArgs a) {
 #undef SVA_LIM
 #undef SVA_SCORE
 #undef SVA_DMA
+#undef SVA_DMA_KB
+#undef SVA_LIM_KB
 #undef SVA_KB
 
     // epilogue: O = O^T / l.  Tile order: padding query rows are written as
