@@ -104,13 +104,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t n) {
 // which the compiled code of every instantiation confirms.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+// The address is a wave-uniform base in SGPRs plus this lane's byte offset
+// (saddr form), so no per-lane 64-bit address arithmetic is spent on it.
+// `base` and `off` must be the same in every lane; readfirstlane keeps the
+// offset (and so the sum) in SGPRs.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lane_off,
+                                          uint32_t lds_addr) {
+    const uint64_t sb = (uint64_t)(uintptr_t)base + __builtin_amdgcn_readfirstlane(off);
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
+        "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(gptr), "s"(lds_addr)
+        : "v"(lane_off), "s"(sb), "s"(lds_addr)
         : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -214,8 +220,11 @@ void attn_kernel(AttnArgs a) {
     const int last_video = p.nB_video - 1;
     const int last_valid = p.blk_valid[last_video];
     // this lane's 16 bytes of every wave-level copy
-    const u32x4_t* kbase = a.k + bh * (int64_t)p.nB * (SPB * CPS) + lane;
-    const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (SPB * CPS) + lane;
+    // this head's K and V tiles (wave-uniform) and this lane's byte offset
+    // in every wave-level copy
+    const u32x4_t* kbase = a.k + bh * (int64_t)p.nB * (SPB * CPS);
+    const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (SPB * CPS);
+    const uint32_t lane_off = (uint32_t)lane * 16u;
     const int nstage = len * SPB;
     if (!DENSE) {
         for (int i = tid; i < len; i += NT) s_col[i] = cl[i];
@@ -256,11 +265,11 @@ void attn_kernel(AttnArgs a) {
     do {                                                                             \
         const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
         const int kb_ = SVA_KB(st_);                                                 \
-        const int64_t off_ = ((int64_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * CPS; \
+        const uint32_t off_ = ((uint32_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * (CPS * 16u); \
         _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
             const int e_ = (i * NWV + wave_u) * 64;                                  \
-            lds_dma16(kbase + off_ + e_, lds_addr(KB_ + e_));                        \
-            lds_dma16(vbase + off_ + e_, lds_addr(VB_ + e_));                        \
+            lds_dma16(kbase, off_ + e_ * 16u, lane_off, lds_addr(KB_ + e_));         \
+            lds_dma16(vbase, off_ + e_ * 16u, lane_off, lds_addr(VB_ + e_));         \
         }                                                                            \
     } while (0)
     // the same two with the stage's block index given (KBI)
@@ -268,11 +277,11 @@ void attn_kernel(AttnArgs a) {
     do {                                                                             \
         const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
         const int kb_ = (KBI);                                                       \
-        const int64_t off_ = ((int64_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * CPS; \
+        const uint32_t off_ = ((uint32_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * (CPS * 16u); \
         _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
             const int e_ = (i * NWV + wave_u) * 64;                                  \
-            lds_dma16(kbase + off_ + e_, lds_addr(KB_ + e_));                        \
-            lds_dma16(vbase + off_ + e_, lds_addr(VB_ + e_));                        \
+            lds_dma16(kbase, off_ + e_ * 16u, lane_off, lds_addr(KB_ + e_));         \
+            lds_dma16(vbase, off_ + e_ * 16u, lane_off, lds_addr(VB_ + e_));         \
         }                                                                            \
     } while (0)
 #define SVA_LIM_KB(st, KBI)                                                          \
@@ -445,16 +454,16 @@ void attn_kernel(AttnArgs a) {
                 const int kb = s_col[i];
                 if (kb >= 0 && kb < p.nB) atomicOr(&s_kept[kb >> 5], 1u << (kb & 31));
             }
-            const u32x4_t* kmb = a.km + bh * (int64_t)ng * CPS + lane;
-            const u32x4_t* vmb = a.vm + bh * (int64_t)ng * CPS + lane;
+            const u32x4_t* kmb = a.km + bh * (int64_t)ng * CPS;
+            const u32x4_t* vmb = a.vm + bh * (int64_t)ng * CPS;
             const float bias_blk = __log2f((float)BLK) / c;
             const float bias_last = __log2f((float)last_valid) / c;
             auto copy = [&](int cg, u32x4_t* KB, u32x4_t* VB) {
 #pragma unroll
                 for (int i = 0; i < LPW; ++i) {
                     const int e = (i * NWV + wave_u) * 64;
-                    lds_dma16(kmb + (int64_t)cg * CPS + e, lds_addr(KB + e));
-                    lds_dma16(vmb + (int64_t)cg * CPS + e, lds_addr(VB + e));
+                    lds_dma16(kmb, (uint32_t)(cg * CPS + e) * 16u, lane_off, lds_addr(KB + e));
+                    lds_dma16(vmb, (uint32_t)(cg * CPS + e) * 16u, lane_off, lds_addr(VB + e));
                 }
             };
             auto stage = [&](int cg, const u32x4_t* KB, const u32x4_t* VB) {
