@@ -379,6 +379,36 @@ def test_deterministic(name):
         assert np.array_equal(run.buf.col.cpu().numpy(), ca)
 
 
+@pytest.mark.parametrize("name", ["comp128", "dense128", "sub64"])
+def test_concurrent_streams(name):
+    """One plan used from two streams at once (default priority), each step
+    with its own inputs and buffers, gives bit for bit what each step gives
+    alone: the plan is read-only after creation."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    plan = run.plan
+    # a second, different input set: Q and K swapped, V negated
+    q2, k2, v2 = dev(k), dev(q), dev(np.ascontiguousarray(v) ^ np.uint16(0x8000))
+    inputs = [(run.q, run.k, run.v, run.wq, run.wk), (q2, k2, v2, run.wk, run.wq)]
+    alone = []
+    for x in inputs:
+        b = S.Buffers(plan)
+        S.forward(plan, *x, b)
+        torch.cuda.synchronize()
+        alone.append(b.o.view(torch.int16).clone())
+    assert not torch.equal(alone[0], alone[1])
+    bufs = [S.Buffers(plan), S.Buffers(plan)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for x, b, st in zip(inputs, bufs, streams):
+            with torch.cuda.stream(st):
+                S.forward(plan, *x, b)
+    torch.cuda.synchronize()
+    for b, want in zip(bufs, alone):
+        assert torch.equal(b.o.view(torch.int16), want)
+
+
 def test_binding_rejects_bad_tensors():
     wl = SMALL["tiny"]
     plan = S.sva_plan_create_ex(S.desc_for(wl))
