@@ -16,10 +16,11 @@
 // layouts written by the reorder kernels (K tiles, V tiles), in which one
 // stage of K and one stage of V are each a contiguous span of 32·d bf16.
 // They are copied into LDS as they are, with global_load_lds_dwordx4 (each
-// wave-level load moves 1 KB, lane l to byte 16 l), into three rotating
-// buffer pairs: the loads for stage st + 2 are issued before stage st is
-// computed, and an iteration ends by waiting for stage st + 1 only (vmcnt;
-// the loads of st + 2 stay in flight) and one barrier.  Per stage each wave
+// wave-level load moves 1 KB, lane l to byte 16 l), into rotating K and V
+// buffers (four of each with 128-token blocks, three and two with 64): the
+// copies for later stages are issued before a stage is computed, and an
+// iteration ends by waiting only for the stages the next iteration reads
+// (vmcnt; later copies stay in flight) and one barrier.  Per stage each wave
 // computes
 //   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries; the
 //                    operand of lane l for channel step s is the 16 bytes at
@@ -135,16 +136,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left unconstrained.
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
-// Stage buffer pairs (K and V, 2·32·d bf16 each): four, so the copies run
-// three stages ahead, while two workgroups of a CU still fit in its LDS.
-// With d = 128 and 64-token blocks a workgroup has only two waves; there
-// three pairs (48 KB) let three workgroups share a CU.
-#ifndef SVA_STAGE_BUFFERS
-#define SVA_STAGE_BUFFERS 4
-#endif
-constexpr int attn_stage_buffers(int d, int blk) {
-    return (d == 128 && blk == 64) ? 3 : SVA_STAGE_BUFFERS;
-}
+// Stage buffers of K and of V (32·d bf16 each).  K of stage st+1 is read in
+// iteration st and V of stage st in iteration st, so with copies at least
+// one iteration ahead K needs three buffers and V two.  With 128-token
+// blocks: four of each (copies up to three stages ahead; two workgroups of
+// four waves fill a CU's registers).  With 64-token blocks a workgroup has
+// only two waves: three K and two V buffers (40 KB at d = 128) let four
+// workgroups, the register limit, share a CU (three with 48 KB).
+constexpr int attn_k_buffers(int, int blk) { return blk == 64 ? 3 : 4; }
+constexpr int attn_v_buffers(int, int blk) { return blk == 64 ? 2 : 4; }
+constexpr int attn_gcd(int a, int b) { return b == 0 ? a : attn_gcd(b, a % b); }
 // waves per SIMD the register budget is sized for (LDS decides the rest):
 // two, i.e. at most 256 registers.  Allowed more, the 64-token-block kernel
 // spreads into AGPRs (238 registers) and runs 3 % slower.
@@ -169,16 +170,23 @@ void attn_kernel(AttnArgs a) {
     constexpr int DT = D / 32;           // 32-channel tiles (O^T rows)
     constexpr float kTau = 8.0f;         // lazy-rescale threshold (log2 units)
     static_assert(LPW >= 1 && LPW * 64 * NWV == CPS, "stage copy split");
-    constexpr int NBUF = attn_stage_buffers(D, BLK);   // copies run NBUF-1 stages ahead
-    static_assert(NBUF >= 3, "K of stage st+1 is read in iteration st");
-    // vmcnt((NBUF-3)·2·LPW): all but the copies of the NBUF-3 latest stages have landed
-    constexpr int kInFlight = (NBUF - 3) * 2 * LPW;
+    constexpr int NBK = attn_k_buffers(D, BLK);   // K copies run NBK-1 stages ahead
+    constexpr int NBV = attn_v_buffers(D, BLK);   // V copies run NBV-1 stages ahead
+    static_assert(NBK >= 3 && NBV >= 2 && NBV <= NBK, "stage buffers");
+    constexpr int NU = NBK / attn_gcd(NBK, NBV) * NBV;   // loop unrolling: buffer indices constant
+    static_assert(NU % SPB == 0, "a loop body covers whole blocks");
+    // list entries a loop body touches (its stages and the copies it issues)
+    constexpr int NE = (NU + NBK - 2) / SPB + 1;
+    // At the end of iteration st, K of stage st+2 and V of stage st+1 must
+    // have landed; they were issued in iterations st+3-NBK and st+2-NBV, so
+    // the copies of the min(NBK-3, NBV-2) latest iterations may stay in flight.
+    constexpr int kInFlight = (NBK - 3 < NBV - 2 ? NBK - 3 : NBV - 2) * 2 * LPW;
     static_assert(kInFlight < 64, "vmcnt range");
     constexpr int kWaitNext = (kInFlight & 15) | ((kInFlight >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-    __shared__ u32x4_t sK[NBUF][CPS];
-    __shared__ u32x4_t sV[NBUF][CPS];
-    extern __shared__ int32_t s_col[];   // this row's block list (sparse plans),
-                                         // then a bitmap of it (compensation)
+    __shared__ u32x4_t sK[NBK][CPS];
+    __shared__ u32x4_t sV[NBV][CPS];
+    extern __shared__ int32_t s_col[];   // compensation: this row's block list,
+                                         // then a bitmap of it
 
     const DevPlan& p = a.p;
     const int ngrp = (p.nB + QPW - 1) / QPW;
@@ -188,6 +196,7 @@ void attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
     // First query block of the group.  Sparse plans start each head with
     // the blocks of extra tokens: their rows keep every block and are the
     // longest, so they must not be the last to begin.
@@ -195,10 +204,11 @@ void attn_kernel(AttnArgs a) {
     const int qfirst = QPW == 1 ? (qg < nx ? p.nB_video + qg : qg - nx) : qg * QPW;
     // this wave's query block; past the last block (odd nB, QPW = 2) the
     // wave computes on the last block's rows and stores nothing
-    const bool q_ok = qfirst + wave / WPB < p.nB;
-    const int qb = q_ok ? qfirst + wave / WPB : p.nB - 1;
+    // (wave-uniform; readfirstlane tells the compiler, so the row's pointers
+    // and lengths stay scalar)
+    const bool q_ok = qfirst + wave_u / WPB < p.nB;
+    const int qb = __builtin_amdgcn_readfirstlane(q_ok ? qfirst + wave_u / WPB : p.nB - 1);
     const int qrow = (wave % WPB) * 32 + j;   // query row within the block
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
 
     // Q^T operand: lane (j, hf) holds channels 16s + 8hf .. +8 of row qrow
     bf16x8_t qop[DS];
@@ -224,6 +234,11 @@ void attn_kernel(AttnArgs a) {
     const int64_t r0 = p.row_ptr[qb];
     const int len = DENSE ? p.nB : (int)(p.row_ptr[qb + 1] - r0);
     const int32_t* cl = DENSE ? nullptr : a.col + bh * p.nnz_per_head + r0;
+    // the same list through the constant address space: wave-uniform
+    // lookups become scalar loads, which do not count against vmcnt (a
+    // vector load would make every wait for it wait for the copies too)
+    const __attribute__((address_space(4))) int32_t* cls =
+        (const __attribute__((address_space(4))) int32_t*)cl;
     const int last_video = p.nB_video - 1;
     const int last_valid = p.blk_valid[last_video];
     // this lane's 16 bytes of every wave-level copy
@@ -233,7 +248,9 @@ void attn_kernel(AttnArgs a) {
     const u32x4_t* vbase = a.vt + bh * (int64_t)p.nB * (SPB * CPS);
     const uint32_t lane_off = (uint32_t)lane * 16u;
     const int nstage = len * SPB;
-    if (!DENSE) {
+    // the block list is read from global memory (wave-uniform lookups, a few
+    // per loop body); only compensation keeps a copy in LDS for its bitmap
+    if constexpr (COMP) {
         for (int i = tid; i < len; i += NT) s_col[i] = cl[i];
         __syncthreads();
     }
@@ -250,7 +267,7 @@ void attn_kernel(AttnArgs a) {
             rot = kstart < len ? kstart : 0;
         } else {
             int cnt = 0;
-            for (int i = lane; i < len; i += 64) cnt += __popcll(__ballot(s_col[i] < kstart));
+            for (int i = lane; i < len; i += 64) cnt += __popcll(__ballot(cl[i] < kstart));
             rot = __builtin_amdgcn_readfirstlane(cnt);
             if (rot >= len) rot = 0;
         }
@@ -264,31 +281,18 @@ void attn_kernel(AttnArgs a) {
         sq_ = sq_ < nstage ? sq_ : nstage - 1;                                       \
         int li_ = rot + sq_ / SPB;                                                   \
         li_ = li_ >= len ? li_ - len : li_;                                          \
-        const int kq_ = DENSE ? li_ : __builtin_amdgcn_readfirstlane(s_col[li_]);    \
+        const int kq_ = DENSE ? li_ : cls[li_];                                      \
         return (kq_ >= 0 && kq_ < p.nB) ? kq_ : -1;                                  \
     }(st))
-    // copies of stage st into the buffer pair (KB_, VB_)
-#define SVA_DMA(st, KB_, VB_)                                                        \
-    do {                                                                             \
-        const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
-        const int kb_ = SVA_KB(st_);                                                 \
-        const uint32_t off_ = ((uint32_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * (CPS * 16u); \
-        _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
-            const int e_ = (i * NWV + wave_u) * 64;                                  \
-            lds_dma16(kbase, off_ + e_ * 16u, lane_off, lds_addr(KB_ + e_));         \
-            lds_dma16(vbase, off_ + e_ * 16u, lane_off, lds_addr(VB_ + e_));         \
-        }                                                                            \
-    } while (0)
-    // the same two with the stage's block index given (KBI)
-#define SVA_DMA_KB(st, KBI, KB_, VB_)                                                \
+    // copies of stage st (block index KBI) from BASE_ into the buffer BUF_
+#define SVA_DMA_KB(st, KBI, BASE_, BUF_)                                             \
     do {                                                                             \
         const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
         const int kb_ = (KBI);                                                       \
         const uint32_t off_ = ((uint32_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * (CPS * 16u); \
         _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
             const int e_ = (i * NWV + wave_u) * 64;                                  \
-            lds_dma16(kbase, off_ + e_ * 16u, lane_off, lds_addr(KB_ + e_));         \
-            lds_dma16(vbase, off_ + e_ * 16u, lane_off, lds_addr(VB_ + e_));         \
+            lds_dma16(BASE_, off_ + e_ * 16u, lane_off, lds_addr(BUF_ + e_));        \
         }                                                                            \
     } while (0)
 #define SVA_LIM_KB(st, KBI)                                                          \
@@ -381,9 +385,9 @@ void attn_kernel(AttnArgs a) {
     // of stage st while it takes the max of stage st+1.  The matrix
     // instructions of one half have no dependence on the vector
     // instructions beside them, so one wave keeps both pipes busy.
-    // Copies run NBUF-1 stages ahead; at the end of iteration st both
-    // buffers of stage st+2 have landed (K of st+2 is read in iteration
-    // st+1).  The loop has no ordinary LDS stores, only copies: after this
+    // K copies run NBK-1 and V copies NBV-1 stages ahead; at the end of
+    // iteration st, K of stage st+2 and V of stage st+1 (both read in
+    // iteration st+1) have landed.  The loop has no ordinary LDS stores, only copies: after this
     // wave's wait, a bare s_barrier makes every wave's part visible and
     // orders every wave's reads of the oldest buffers before the copies
     // into them.  (__syncthreads() would add a workgroup release fence,
@@ -394,8 +398,10 @@ void attn_kernel(AttnArgs a) {
     bf16x8_t pb[2];
     if (nstage > 0) {
 #pragma unroll
-        for (int u = 0; u < NBUF - 1; ++u) SVA_DMA(u, sK[u], sV[u]);
-        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        for (int u = 0; u < NBK - 1; ++u) SVA_DMA_KB(u, SVA_KB(u), kbase, sK[u]);
+#pragma unroll
+        for (int u = 0; u < NBV - 1; ++u) SVA_DMA_KB(u, SVA_KB(u), vbase, sV[u]);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __builtin_amdgcn_s_barrier();
         const int lim0 = SVA_LIM(0);
         SVA_SCORE(sK[0], sc);
@@ -404,34 +410,27 @@ void attn_kernel(AttnArgs a) {
         mx = lane_swap_max(mx) * c;
         SVA_RESCALE(mx);
     }
-    // unrolled by NBUF so every buffer index is a constant
-    for (int st = 0; st < nstage; st += NBUF) {
-        // With NBUF == SPB the body's stages st .. st+SPB-1 are one list
-        // entry and the next SPB stages the next one (nstage is a multiple of
-        // SPB, so either all of them exist or all clamp to the last stage):
-        // two block-index lookups per body instead of two per stage.
-        int kbA = 0, kbB = 0;
-        if constexpr (NBUF == SPB) {
-            kbA = SVA_KB(st);
-            kbB = SVA_KB(st + SPB);
-        }
+    // unrolled by NU (a multiple of NBK, NBV and SPB) so every buffer index
+    // is a constant and a body covers whole list entries
+    for (int st = 0; st < nstage; st += NU) {
+        // The block of every stage the body touches: stages st + e·SPB ..
+        // + SPB - 1 are list entry e of the body (nstage is a multiple of
+        // SPB, so either all of them exist or all clamp to the last stage),
+        // so NE lookups per body instead of two per stage.
+        int kbE[NE];
 #pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
+        for (int e = 0; e < NE; ++e) kbE[e] = SVA_KB(st + e * SPB);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
             if (u == 0 || st + u < nstage) {
-                int lim;
-                if constexpr (NBUF == SPB) {
-                    SVA_DMA_KB(st + u + NBUF - 1, u == 0 ? kbA : kbB, sK[(u + NBUF - 1) % NBUF],
-                               sV[(u + NBUF - 1) % NBUF]);
-                    lim = SVA_LIM_KB(st + u + 1, u < NBUF - 1 ? kbA : kbB);
-                } else {
-                    SVA_DMA(st + u + NBUF - 1, sK[(u + NBUF - 1) % NBUF], sV[(u + NBUF - 1) % NBUF]);
-                    lim = SVA_LIM(st + u + 1);
-                }
+                SVA_DMA_KB(st + u + NBK - 1, kbE[(u + NBK - 1) / SPB], kbase, sK[(u + NBK - 1) % NBK]);
+                SVA_DMA_KB(st + u + NBV - 1, kbE[(u + NBV - 1) / SPB], vbase, sV[(u + NBV - 1) % NBV]);
+                const int lim = SVA_LIM_KB(st + u + 1, kbE[(u + 1) / SPB]);
                 // one straight-line region: the scheduler interleaves the
                 // matrix and vector halves
-                SVA_SCORE(sK[(u + 1) % NBUF], sn);
+                SVA_SCORE(sK[(u + 1) % NBK], sn);
                 SVA_EXP(sc, pb);
-                SVA_PV(sV[u], pb);
+                SVA_PV(sV[u % NBV], pb);
                 SVA_MAX(sn, mx);
                 SVA_MASK(lim, sn, mx);
                 mx = lane_swap_max(mx) * c;
@@ -517,7 +516,6 @@ void attn_kernel(AttnArgs a) {
 #undef SVA_MAX
 #undef SVA_LIM
 #undef SVA_SCORE
-#undef SVA_DMA
 #undef SVA_DMA_KB
 #undef SVA_LIM_KB
 #undef SVA_KB
@@ -573,8 +571,8 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
     const int qpw = (p.dense && !(p.d == 64 && p.block == 128)) ? 2 : 1;
     dim3 grid((unsigned)((int64_t)p.B * p.H * ((p.nB + qpw - 1) / qpw)));
     dim3 block(p.block * 2 * qpw);
-    const size_t lds = p.dense ? 0
-                     : (size_t)(p.max_row_len + (km ? p.n_mean_groups : 0)) * sizeof(int32_t);
+    // dynamic LDS: compensation's copy of the block list and its bitmap
+    const size_t lds = km ? (size_t)(p.max_row_len + p.n_mean_groups) * sizeof(int32_t) : 0;
     auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, lds, s, a); };
     // dense plans have nothing to compensate; compensation is its own
     // instantiation so the plain kernels carry none of it
