@@ -63,6 +63,11 @@ SMALL = {
     # an odd number of blocks, extra tokens, B = 2
     "dense_d128_b64": I.custom("dense_d128_b64", 2, 2, 3, 10, 14, 128, 64, 0.0, tile=(2, 4, 8),
                                n_extra=128, seed_base=10300),
+    # degenerate sizes: a single (clipped) block; sparsity 0.99, one ranked
+    # block per row beside the same-frame and extra-token ones
+    "single": I.custom("single", 1, 2, 1, 4, 8, 64, 64, 0.5, tile=(4, 4, 4), seed_base=10400),
+    "sparse99": I.custom("sparse99", 2, 2, 4, 16, 24, 128, 128, 0.99,
+                         flags=I.KEEP_SAME_FRAME, n_extra=128, seed_base=10500),
 }
 
 
