@@ -455,21 +455,18 @@ def _full_inputs(wl):
     return _full_cache[key]
 
 
-@pytest.mark.slow
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", FULL)
-def test_full_workload_sampled(name):
-    wl = I.WORKLOADS[name]
+def _check_step(wl, q, k, v, wq, wk, heads, qbs, b=0):
+    """The whole step on the GPU (staged, then fused) against the oracle for
+    batch b, the given heads and query blocks: prologue, reorders (bit-exact
+    from the GPU's own prologue output), masks from the GPU's own Q' and K'
+    (exact up to counted ties), attention on identical inputs, the chained
+    step from the raw inputs, and the fused step equal to the staged one."""
+    name = wl.name
     g = geometry(wl)
-    q, k, v, wq, wk = _full_inputs(wl)
-    print(f"{name}: inputs ready", flush=True)
     run = GpuRun(wl, q, k, v, wq, wk).run()
     perm = O.permutation(g)
     meta = O.block_meta(g, perm)
     forced, dense_row = O.forced_blocks(g, meta)
-    rng = np.random.default_rng(wl.seed_base + 7)
-    heads = sorted({0, wl.H - 1, int(rng.integers(0, wl.H))})
-    qbs = sorted({0, g.nB_video - 1, g.nB - 1, *rng.integers(0, g.nB, 5).tolist()})
     _, row_ptr, _ = run.plan.host_tables()
     nnz = int(run.plan.info.nnz_per_head)
     col = run.buf.col.cpu().numpy() if run.buf.col is not None else None
@@ -478,12 +475,12 @@ def test_full_workload_sampled(name):
     worst = dict(att_rel=0.0, att_abs=0.0, ch_rel=0.0, ch_abs=0.0)
     for h in heads:
         print(f"{name}: checking head {h}", flush=True)
-        qh = O.bf16_bits_to_f64(q[0, :, h])
-        kh = O.bf16_bits_to_f64(k[0, :, h])
-        vh = O.bf16_bits_to_f64(v[0, :, h])
+        qh = O.bf16_bits_to_f64(q[b, :, h])
+        kh = O.bf16_bits_to_f64(k[b, :, h])
+        vh = O.bf16_bits_to_f64(v[b, :, h])
         # prologue
-        qn_g = host(run.buf.qn[0, :, h])
-        kn_g = host(run.buf.kn[0, :, h])
+        qn_g = host(run.buf.qn[b, :, h])
+        kn_g = host(run.buf.kn[b, :, h])
         for got, x, w in ((qn_g, qh, wq[h]), (kn_g, kh, wk[h])):
             rep = []
             ok, n, t = prologue_check(x, w, g, got, rep)
@@ -492,9 +489,9 @@ def test_full_workload_sampled(name):
             stats["ulp_mism"] += n
             stats["elems"] += t
         # reorder (bit-exact, from the GPU's own prologue output)
-        qr_g = host(run.buf.q_r[0, h])
-        kt_g = host(run.buf.k_t[0, h])
-        vt_g = host(run.buf.v_t[0, h])
+        qr_g = host(run.buf.q_r[b, h])
+        kt_g = host(run.buf.k_t[b, h])
+        vt_g = host(run.buf.v_t[b, h])
         want = np.zeros((g.Np, g.d), np.uint16)
         want[perm] = qn_g
         if not np.array_equal(qr_g, want):
@@ -503,7 +500,7 @@ def test_full_workload_sampled(name):
         kr_g = want.copy()
         if not np.array_equal(kt_g, _kt_from_kr(want, g)):
             fails.append(("reorder k tiles", h))
-        want[perm] = v[0, :, h]
+        want[perm] = v[b, :, h]
         if not np.array_equal(vt_g, _vt_from_vr(want, g)):
             fails.append(("reorder v tiles", h))
         vr_f = O.bf16_bits_to_f64(want)
@@ -518,7 +515,7 @@ def test_full_workload_sampled(name):
             else:
                 kept_ref, scores, thresh, smax = O.select_blocks(
                     O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]), g, meta)
-            kept_g = kept_from_col(col[h * nnz:(h + 1) * nnz], row_ptr, g.nB)
+            kept_g = kept_from_col(col[(b * wl.H + h) * nnz:(b * wl.H + h + 1) * nnz], row_ptr, g.nB)
             n, e = compare_masks(kept_g, kept_ref, scores, thresh, smax, forced)
             stats["mask_diffs"] += n
             stats["mask_excused"] += e
@@ -526,13 +523,13 @@ def test_full_workload_sampled(name):
             kept_g = np.ones((g.nB, g.nB), bool)
         # attention on identical inputs and the GPU's block list
         o_ref = O.block_attention(qr_f, kr_f, vr_f, kept_g, g, meta, qblocks=qbs)
-        o_g = host_f64(run.buf.o_r[0, h])
-        rows = np.concatenate([np.arange(b * g.block, (b + 1) * g.block) for b in qbs])
+        o_g = host_f64(run.buf.o_r[b, h])
+        rows = np.concatenate([np.arange(qb * g.block, (qb + 1) * g.block) for qb in qbs])
         worst["att_rel"] = max(worst["att_rel"], rel_l2(o_g[rows], o_ref[rows]))
         worst["att_abs"] = max(worst["att_abs"], max_abs(o_g[rows], o_ref[rows]))
         # inverse reorder of O (bit-exact)
-        o_rast = host(run.buf.o[0, :, h])
-        if not np.array_equal(o_rast, host(run.buf.o_r[0, h])[perm]):
+        o_rast = host(run.buf.o[b, :, h])
+        if not np.array_equal(o_rast, host(run.buf.o_r[b, h])[perm]):
             fails.append(("reorder inverse", h))
         # chained: the oracle from the raw inputs
         r = O.run_head(qh, kh, vh, wq[h], wk[h], g, qblocks=qbs, perm=perm, meta=meta)
@@ -549,3 +546,69 @@ def test_full_workload_sampled(name):
     assert stats["mask_diffs"] == stats["mask_excused"]
     assert worst["att_rel"] <= REL_L2 and worst["att_abs"] <= MAX_ABS
     assert worst["ch_rel"] <= REL_L2 and worst["ch_abs"] <= MAX_ABS
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled(name):
+    wl = I.WORKLOADS[name]
+    g = geometry(wl)
+    q, k, v, wq, wk = _full_inputs(wl)
+    print(f"{name}: inputs ready", flush=True)
+    rng = np.random.default_rng(wl.seed_base + 7)
+    heads = sorted({0, wl.H - 1, int(rng.integers(0, wl.H))})
+    qbs = sorted({0, g.nB_video - 1, g.nB - 1, *rng.integers(0, g.nB, 5).tolist()})
+    _check_step(wl, q, k, v, wq, wk, heads, qbs)
+
+
+def _random_workloads(n, seed=20250):
+    """Seeded random small shapes over every plan option the library has."""
+    rng = np.random.default_rng(seed)
+    tiles = {64: [(4, 4, 4), (2, 4, 8), (1, 8, 8), (4, 2, 8), (1, 4, 16)],
+             128: [(2, 8, 8), (4, 4, 8), (2, 4, 16), (1, 8, 16)]}
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        block = int(rng.choice([64, 128]))
+        tile = tiles[block][int(rng.integers(len(tiles[block])))]
+        T, Hh, W = (int(rng.integers(1, 9)), int(rng.integers(3, 34)), int(rng.integers(3, 50)))
+        sparsity = float(rng.choice([0.0, 0.3, 0.5, 0.75, 0.9]))
+        flags = 0
+        if rng.random() < 0.15:
+            flags |= I.DENSE
+        if rng.random() < 0.4:
+            flags |= I.KEEP_SAME_FRAME
+        if rng.random() < 0.25 and sparsity > 0 and not flags & I.DENSE:
+            flags |= I.COMPENSATE
+        n_extra = int(block * rng.integers(0, 2))
+        scorer = int(rng.random() < 0.3)
+        subblocks = int(rng.choice([1, 2, 4])) if scorer else 0
+        budget_multiple = int(rng.choice([0, 8])) if scorer else 0
+        split = (0, 0, 0)
+        if rng.random() < 0.25:
+            split = (16, 16, 16) if d == 64 else (32, 32, 32)
+        wl = I.custom(f"random{len(out)}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), T, Hh, W,
+                      d, block, sparsity, flags=flags, tile=tile, n_extra=n_extra,
+                      temperature=bool(rng.random() < 0.5), seed_base=30000 + 100 * len(out),
+                      rope_split=split, scorer=scorer, subblocks=subblocks,
+                      budget_multiple=budget_multiple)
+        try:
+            S.sva_plan_query(S.desc_for(wl))
+        except S.SvaError:
+            continue
+        out.append(wl)
+    return out
+
+
+RANDOM = _random_workloads(12)
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=lambda w: w.name)
+def test_random_shapes(wl):
+    """Random small shapes through the whole step, every head and query
+    block of the last batch checked against the oracle."""
+    q, k, v, wq, wk = workload_inputs(wl)
+    g = geometry(wl)
+    print(f"{wl}", flush=True)
+    _check_step(wl, q, k, v, wq, wk, list(range(wl.H)), list(range(g.nB)), b=wl.B - 1)
