@@ -127,6 +127,21 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
         : "v"(lane_off), "s"(sb), "s"(lds_addr)
         : "memory", "m0");
 }
+// The same copy from a wave-uniform base pointer (SGPRs) and this lane's
+// byte offset; the LDS destination is a wave-uniform base plus a constant,
+// added into M0 in the same block (the add is the wait state the load needs
+// after the M0 write is not: one s_nop remains).
+// `imm` must fold to a constant once the caller's loops are unrolled.
+__device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t lane_off,
+                                             uint32_t lds_base, uint32_t imm) {
+    asm volatile(
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(lane_off), "s"(base), "s"(lds_base), "i"(imm)
+        : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -273,33 +288,46 @@ void attn_kernel(AttnArgs a) {
         }
     }
 
-    // block of stage st (clamped into the row so copies past the end stay in
-    // valid memory; list entry (rot + st/SPB) mod len); -1 marks an
-    // out-of-range list entry
-#define SVA_KB(st)                                                                   \
-    ([&](int sq_) {                                                                  \
-        sq_ = sq_ < nstage ? sq_ : nstage - 1;                                       \
-        int li_ = rot + sq_ / SPB;                                                   \
-        li_ = li_ >= len ? li_ - len : li_;                                          \
-        const int kq_ = DENSE ? li_ : cls[li_];                                      \
-        return (kq_ >= 0 && kq_ < p.nB) ? kq_ : -1;                                  \
-    }(st))
-    // copies of stage st (block index KBI) from BASE_ into the buffer BUF_
-#define SVA_DMA_KB(st, KBI, BASE_, BUF_)                                             \
+    // List entry w of the walk (w = 0 .. len-1 is list index (rot + w) mod
+    // len): the byte offset of its block in this head's K and V tiles, and
+    // its number of valid keys.  Entries past the end of the row and
+    // out-of-range list entries have no valid keys; their copies read block
+    // 0 into buffers that are never read, so every iteration issues the same
+    // copies and the copy data always stays inside the head's tiles.
+    struct Ent { uint32_t off; int nv; };
+    auto entry = [&](int w) {
+        const bool in = w < len;
+        int li = rot + (in ? w : len - 1);
+        li = li >= len ? li - len : li;
+        const int kq = DENSE ? li : cls[li];
+        const bool ok = in && kq >= 0 && kq < p.nB;
+        Ent r;
+        r.off = (uint32_t)(ok ? kq : 0) * (uint32_t)(SPB * CPS * 16);
+        r.nv = ok ? (kq == last_video ? last_valid : BLK) : 0;
+        return r;
+    };
+    // this lane's byte offset in copy i of stage q of a block (constants)
+    uint32_t loff[SPB][LPW];
+#pragma unroll
+    for (int q = 0; q < SPB; ++q)
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            loff[q][i] = (uint32_t)((q * CPS + (i * NWV + wave_u) * 64) * 16) + lane_off;
+    const uint32_t kl0 = lds_addr(&sK[0][0]) + (uint32_t)wave_u * 1024u;
+    const uint32_t vl0 = lds_addr(&sV[0][0]) + (uint32_t)wave_u * 1024u;
+    // copies of stage Q_ of the block at PTR_ into K buffer BUF_ (resp. V)
+#define SVA_COPY_K(PTR_, Q_, BUF_)                                                   \
     do {                                                                             \
-        const int st_ = (st) < nstage ? (st) : nstage - 1;                           \
-        const int kb_ = (KBI);                                                       \
-        const uint32_t off_ = ((uint32_t)(kb_ < 0 ? 0 : kb_) * SPB + (st_ % SPB)) * (CPS * 16u); \
-        _Pragma("unroll") for (int i = 0; i < LPW; ++i) {                            \
-            const int e_ = (i * NWV + wave_u) * 64;                                  \
-            lds_dma16(BASE_, off_ + e_ * 16u, lane_off, lds_addr(BUF_ + e_));        \
-        }                                                                            \
+        _Pragma("unroll") for (int i = 0; i < LPW; ++i)                              \
+            lds_dma16_at(PTR_, loff[Q_][i], kl0,                                   \
+                         (uint32_t)(((BUF_) * CPS + i * NWV * 64) * 16));            \
     } while (0)
-#define SVA_LIM_KB(st, KBI)                                                          \
-    ([&](int sl_, int kb_) {                                                         \
-        return (sl_ >= nstage || kb_ < 0) ? 0                                        \
-             : (kb_ == last_video ? min(last_valid - (sl_ % SPB) * SK, SK) : SK);    \
-    }(st, KBI))
+#define SVA_COPY_V(PTR_, Q_, BUF_)                                                   \
+    do {                                                                             \
+        _Pragma("unroll") for (int i = 0; i < LPW; ++i)                              \
+            lds_dma16_at(PTR_, loff[Q_][i], vl0,                                   \
+                         (uint32_t)(((BUF_) * CPS + i * NWV * 64) * 16));            \
+    } while (0)
     // S^T of stage st into SC from the K buffer KB_
 #define SVA_SCORE(KB_, SC)                                                           \
     do {                                                                             \
@@ -308,13 +336,6 @@ void attn_kernel(AttnArgs a) {
             SC = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(KB_[s * 64 + lane]), \
                                                          qop[s], SC, 0, 0, 0);       \
     } while (0)
-    // number of valid keys of stage st (0 for stages past the end)
-#define SVA_LIM(st)                                                                  \
-    ([&](int sl_) {                                                                  \
-        const int kb_ = SVA_KB(sl_);                                                 \
-        return (sl_ >= nstage || kb_ < 0) ? 0                                        \
-             : (kb_ == last_video ? min(last_valid - (sl_ % SPB) * SK, SK) : SK);    \
-    }(st))
     // row max of SC over every key
 #define SVA_MAX(SC, MX)                                                              \
     do {                                                                             \
@@ -396,49 +417,60 @@ void attn_kernel(AttnArgs a) {
     f32x16_t sc, sn;
     float mx;
     bf16x8_t pb[2];
+    constexpr int NUE = NU / SPB;        // list entries per loop body
+    constexpr int NC = NE - NUE;         // entries a body hands to the next
+    static_assert(NC >= 1, "entry carry");
+    const char* kb8 = reinterpret_cast<const char*>(kbase);
+    const char* vb8 = reinterpret_cast<const char*>(vbase);
+    Ent C[NC];
+#pragma unroll
+    for (int e = 0; e < NC; ++e) C[e] = entry(e);
     if (nstage > 0) {
+        Ent E[NE];
 #pragma unroll
-        for (int u = 0; u < NBK - 1; ++u) SVA_DMA_KB(u, SVA_KB(u), kbase, sK[u]);
+        for (int e = 0; e < NE; ++e) E[e] = e < NC ? C[e] : entry(e);
 #pragma unroll
-        for (int u = 0; u < NBV - 1; ++u) SVA_DMA_KB(u, SVA_KB(u), vbase, sV[u]);
+        for (int u = 0; u < NBK - 1; ++u) SVA_COPY_K(kb8 + E[u / SPB].off, u % SPB, u);
+#pragma unroll
+        for (int u = 0; u < NBV - 1; ++u) SVA_COPY_V(vb8 + E[u / SPB].off, u % SPB, u);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __builtin_amdgcn_s_barrier();
-        const int lim0 = SVA_LIM(0);
         SVA_SCORE(sK[0], sc);
         SVA_MAX(sc, mx);
-        SVA_MASK(lim0, sc, mx);
+        SVA_MASK(E[0].nv, sc, mx);
         mx = lane_swap_max(mx) * c;
         SVA_RESCALE(mx);
     }
-    // unrolled by NU (a multiple of NBK, NBV and SPB) so every buffer index
-    // is a constant and a body covers whole list entries
-    for (int st = 0; st < nstage; st += NU) {
-        // The block of every stage the body touches: stages st + e·SPB ..
-        // + SPB - 1 are list entry e of the body (nstage is a multiple of
-        // SPB, so either all of them exist or all clamp to the last stage),
-        // so NE lookups per body instead of two per stage.
-        int kbE[NE];
+    // A body covers NUE whole list entries (NU stages, a multiple of NBK,
+    // NBV and SPB, so every buffer index is a constant).  It needs the
+    // entries w .. w+NE-1: the first NC come from the previous body, the
+    // rest are looked up (scalar loads) once.
+    for (int w = 0; w < len; w += NUE) {
+        Ent E[NE];
 #pragma unroll
-        for (int e = 0; e < NE; ++e) kbE[e] = SVA_KB(st + e * SPB);
+        for (int e = 0; e < NE; ++e) E[e] = e < NC ? C[e] : entry(w + e);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) C[e] = E[e + NUE];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            if (u == 0 || st + u < nstage) {
-                SVA_DMA_KB(st + u + NBK - 1, kbE[(u + NBK - 1) / SPB], kbase, sK[(u + NBK - 1) % NBK]);
-                SVA_DMA_KB(st + u + NBV - 1, kbE[(u + NBV - 1) / SPB], vbase, sV[(u + NBV - 1) % NBV]);
-                const int lim = SVA_LIM_KB(st + u + 1, kbE[(u + 1) / SPB]);
-                // one straight-line region: the scheduler interleaves the
-                // matrix and vector halves
-                SVA_SCORE(sK[(u + 1) % NBK], sn);
-                SVA_EXP(sc, pb);
-                SVA_PV(sV[u % NBV], pb);
-                SVA_MAX(sn, mx);
-                SVA_MASK(lim, sn, mx);
-                mx = lane_swap_max(mx) * c;
-                SVA_RESCALE(mx);
-                sc = sn;
-                __builtin_amdgcn_s_waitcnt(kWaitNext);
-                __builtin_amdgcn_s_barrier();
-            }
+            // a body's later entries may lie past the end of the row
+            if (u > 0 && u % SPB == 0 && w + u / SPB >= len) break;
+            const int ck = u + NBK - 1, cv = u + NBV - 1, cs = u + 1;
+            SVA_COPY_K(kb8 + E[ck / SPB].off, ck % SPB, ck % NBK);
+            SVA_COPY_V(vb8 + E[cv / SPB].off, cv % SPB, cv % NBV);
+            const int lim = E[cs / SPB].nv - (cs % SPB) * SK;
+            // one straight-line region: the scheduler interleaves the
+            // matrix and vector halves
+            SVA_SCORE(sK[cs % NBK], sn);
+            SVA_EXP(sc, pb);
+            SVA_PV(sV[u % NBV], pb);
+            SVA_MAX(sn, mx);
+            SVA_MASK(lim, sn, mx);
+            mx = lane_swap_max(mx) * c;
+            SVA_RESCALE(mx);
+            sc = sn;
+            __builtin_amdgcn_s_waitcnt(kWaitNext);
+            __builtin_amdgcn_s_barrier();
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // no copy left in flight at exit
@@ -514,11 +546,9 @@ void attn_kernel(AttnArgs a) {
 #undef SVA_RESCALE
 #undef SVA_MASK
 #undef SVA_MAX
-#undef SVA_LIM
 #undef SVA_SCORE
-#undef SVA_DMA_KB
-#undef SVA_LIM_KB
-#undef SVA_KB
+#undef SVA_COPY_K
+#undef SVA_COPY_V
 
     // epilogue: O = O^T / l.  Tile order: padding query rows are written as
     // zeros.  Raster order: row qrow goes to raster token inv[qb·BLK + qrow]
