@@ -184,6 +184,7 @@ void attn_kernel(AttnArgs a) {
     constexpr int DS = D / 16;           // 16-channel steps (S^T contraction)
     constexpr int DT = D / 32;           // 32-channel tiles (O^T rows)
     constexpr float kTau = 8.0f;         // lazy-rescale threshold (log2 units)
+    constexpr float kPmax = 256.0f;      // 2^kTau: the largest probability it allows
     static_assert(LPW >= 1 && LPW * 64 * NWV == CPS, "stage copy split");
     constexpr int NBK = attn_k_buffers(D, BLK);   // K copies run NBK-1 stages ahead
     constexpr int NBV = attn_v_buffers(D, BLK);   // V copies run NBV-1 stages ahead
@@ -389,6 +390,64 @@ void attn_kernel(AttnArgs a) {
             PB[s2] = as_bf16x8(u_);                                                  \
         }                                                                            \
     } while (0)
+    // keys from LIM on to -inf (rare; see SVA_MASK), no max
+#define SVA_MASK_ONLY(LIM, SC)                                                       \
+    do {                                                                             \
+        if (LIM < SK) {                                                              \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) {                         \
+                const int key_ = 8 * (v / 4) + 4 * hf + (v % 4);                     \
+                if (key_ >= LIM) SC[v] = -INFINITY;                                  \
+            }                                                                        \
+        }                                                                            \
+    } while (0)
+#ifndef SVA_ROWSUM_DOT2
+#define SVA_ROWSUM_DOT2 0
+#endif
+    // probabilities of SC against m into PB and their sum into LS
+#define SVA_EXP_SUM(SC, PB, LS)                                                      \
+    do {                                                                             \
+        float e_[16];                                                                \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v)                               \
+            e_[v] = __builtin_amdgcn_exp2f(fmaf(SC[v], c, -m));                      \
+        u32x4_t u_[2];                                                               \
+        _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                           \
+            u_[s2].x = pack_bf16x2(e_[8 * s2 + 0], e_[8 * s2 + 1]);                  \
+            u_[s2].y = pack_bf16x2(e_[8 * s2 + 2], e_[8 * s2 + 3]);                  \
+            u_[s2].z = pack_bf16x2(e_[8 * s2 + 4], e_[8 * s2 + 5]);                  \
+            u_[s2].w = pack_bf16x2(e_[8 * s2 + 6], e_[8 * s2 + 7]);                  \
+            PB[s2] = as_bf16x8(u_[s2]);                                              \
+        }                                                                            \
+        LS = 0.f;                                                                    \
+        if (SVA_ROWSUM_DOT2) {                                                       \
+            const bf16x2_t one_ = {(__bf16)1.0f, (__bf16)1.0f};                      \
+            _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                       \
+                LS = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u_[s2].x), one_, LS, false); \
+                LS = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u_[s2].y), one_, LS, false); \
+                LS = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u_[s2].z), one_, LS, false); \
+                LS = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u_[s2].w), one_, LS, false); \
+            }                                                                        \
+        } else {                                                                     \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) LS += e_[v];              \
+        }                                                                            \
+    } while (0)
+    // Probabilities of stage SC with the lazy rescale decided after the
+    // fact: every probability is at most 2^kTau (up to rounding) when no logit
+    // exceeds the running max by more than kTau, and a probability above
+    // 2^kTau makes the lane's sum exceed it, so only a wave with such a sum
+    // takes the max of the stage, raises m by the usual rule and recomputes.
+#define SVA_EXP_CHECKED(SC, PB)                                                      \
+    do {                                                                             \
+        float ls_;                                                                   \
+        SVA_EXP_SUM(SC, PB, ls_);                                                    \
+        if (__any(ls_ >= kPmax)) {                                                   \
+            float mx_;                                                               \
+            SVA_MAX(SC, mx_);                                                        \
+            mx_ = lane_swap_max(mx_) * c;                                            \
+            SVA_RESCALE(mx_);                                                        \
+            SVA_EXP_SUM(SC, PB, ls_);                                                \
+        }                                                                            \
+        l += ls_;                                                                    \
+    } while (0)
     // O^T += V^T P^T from the V buffer VB_.  Step s2 contracts stage keys
     // 16*s2 + ..; lane half hf's 8 of them are V chunk 2*s2 + hf.
 #define SVA_PV(VB_, PB)                                                              \
@@ -462,12 +521,9 @@ void attn_kernel(AttnArgs a) {
             // one straight-line region: the scheduler interleaves the
             // matrix and vector halves
             SVA_SCORE(sK[cs % NBK], sn);
-            SVA_EXP(sc, pb);
+            SVA_EXP_CHECKED(sc, pb);
             SVA_PV(sV[u % NBV], pb);
-            SVA_MAX(sn, mx);
-            SVA_MASK(lim, sn, mx);
-            mx = lane_swap_max(mx) * c;
-            SVA_RESCALE(mx);
+            SVA_MASK_ONLY(lim, sn);
             sc = sn;
             __builtin_amdgcn_s_waitcnt(kWaitNext);
             __builtin_amdgcn_s_barrier();
@@ -543,6 +599,9 @@ void attn_kernel(AttnArgs a) {
     }
 #undef SVA_PV
 #undef SVA_EXP
+#undef SVA_EXP_SUM
+#undef SVA_EXP_CHECKED
+#undef SVA_MASK_ONLY
 #undef SVA_RESCALE
 #undef SVA_MASK
 #undef SVA_MAX

@@ -236,8 +236,9 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t,
 /* Attention over the kept blocks.  For each valid query row p of block qb:
  * o_p = sum_j softmax_j(q_p·k_j / sqrt(d)) v_j over the valid keys j of the
  * blocks in row qb of `col` (any ascending list with the plan's row_ptr is
- * accepted; entries outside [0, nB) are skipped; a dense plan ignores
- * `col`, which may be NULL).  q_r: [B, H, Np, d] (SVA_FORWARD of Q');
+ * accepted; entries outside [0, nB) are skipped, and a row left with no
+ * valid entry gets zero output; a dense plan ignores `col`, which may be
+ * NULL).  q_r: [B, H, Np, d] (SVA_FORWARD of Q');
  * k_t: K tiles (SVA_FORWARD_KT of K'); v_t: V tiles (SVA_FORWARD_VT of V);
  * o_r: [B, H, Np, d], padding rows written as zero. */
 int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,

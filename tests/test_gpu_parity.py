@@ -242,6 +242,112 @@ def test_attention_parity(name):
     assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
 
 
+# 80 blocks of 64 tokens: query blocks from 64 on start their walk at the
+# first list entry at or after block 64
+OOB = I.custom("oob80", 1, 2, 5, 32, 32, 64, 64, 0.5, tile=(1, 4, 16), seed_base=10600)
+
+
+def test_attention_out_of_range_entries():
+    """List entries outside [0, nB) are skipped: rows that start with
+    negative entries, rows that end with entries past nB, rows whose walk
+    begins on such an entry (every valid entry below the walk's start), and
+    a row with no valid entry at all (zero output)."""
+    wl = OOB
+    q, k, v, wq, wk = workload_inputs(wl)
+    g = geometry(wl)
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    assert g.nB == 80
+    run = GpuRun(wl, q, k, v, wq, wk)
+    _, row_ptr, _ = run.plan.host_tables()
+    B, H = wl.B, wl.H
+    qr = np.zeros((B, H, g.Np, g.d), np.uint16)
+    kt = np.zeros((B, H, g.nB, g.block // 32, g.d // 16, 64, 8), np.uint16)
+    vt = np.zeros((B, H, g.nB, g.block // 32, 4, g.d, 8), np.uint16)
+    cols, refs, kept_all = [], [], []
+    for h in range(H):
+        r = O.run_head(O.bf16_bits_to_f64(q[0, :, h]), O.bf16_bits_to_f64(k[0, :, h]),
+                       O.bf16_bits_to_f64(v[0, :, h]), wq[h], wk[h], g, perm=perm, meta=meta)
+        qr[0, h] = O.f64_to_bf16_bits(r["qr"])
+        kt[0, h] = _kt_from_kr(O.f64_to_bf16_bits(r["kr"]), g)
+        vt[0, h] = _vt_from_vr(O.f64_to_bf16_bits(r["vr"]), g)
+        kept = np.zeros((g.nB, g.nB), bool)
+        col = []
+        n_start_invalid = 0
+        for qb in range(g.nB):
+            lst = sorted(np.nonzero(r["kept"][qb])[0].tolist())
+            assert len(lst) == row_ptr[qb + 1] - row_ptr[qb]
+            if qb == 1:
+                lst = [-len(lst) + i for i in range(len(lst))]          # nothing valid
+            elif qb >= 64:
+                low = [kb for kb in lst if kb < 64]
+                lst = low + [g.nB + i for i in range(len(lst) - len(low))]
+                n_start_invalid += len(low) < len(lst)
+            elif qb % 3 == 0:
+                lst = [-5] + lst[1:]
+            elif qb % 3 == 1:
+                lst = lst[:-1] + [g.nB + 7]
+            for kb in lst:
+                if 0 <= kb < g.nB:
+                    kept[qb, kb] = True
+            col += lst
+        assert n_start_invalid > 0
+        cols.append(np.array(col, np.int32))
+        empty = ~kept.any(axis=1)
+        kept_ok = kept.copy()
+        kept_ok[empty, 0] = True       # any block: those rows are checked as zeros
+        refs.append((O.block_attention(r["qr"], r["kr"], r["vr"], kept_ok, g, meta), empty))
+    S.sva_attention(run.plan, dev(qr), dev(kt), dev(vt), dev_col(np.concatenate(cols)),
+                    run.buf.o_r)
+    torch.cuda.synchronize()
+    out = host_f64(run.buf.o_r)
+    for h, (ref, empty) in enumerate(refs):
+        rows = np.concatenate([np.arange(qb * g.block, (qb + 1) * g.block)
+                               for qb in range(g.nB) if not empty[qb]])
+        zero = np.concatenate([np.arange(qb * g.block, (qb + 1) * g.block)
+                               for qb in range(g.nB) if empty[qb]])
+        assert np.all(out[0, h][zero] == 0)
+        print(f"head {h}: rel_l2 {rel_l2(out[0, h][rows], ref[rows]):.2e} "
+              f"max_abs {max_abs(out[0, h][rows], ref[rows]):.2e}")
+        assert rel_l2(out[0, h][rows], ref[rows]) <= REL_L2
+        assert max_abs(out[0, h][rows], ref[rows]) <= MAX_ABS
+
+
+_GROWTH = ["ragged128", "ragged64", "d128_b64", "dense128"]
+
+
+@pytest.mark.parametrize("name", _GROWTH)
+def test_large_logit_growth(name):
+    """Norm weights of 3 (logits nine times the unit-weight ones): a row's
+    running max grows by far more than the lazy-rescale threshold after its
+    first stage, so the rescale of the accumulators runs many times per row.
+    The inputs are checked to do that (on the CPU, in the walk order of these
+    small heads: list order), then the whole step against the oracle."""
+    wl = SMALL[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    wq = np.full_like(wq, 3.0)
+    wk = np.full_like(wk, 3.0)
+    g = geometry(wl)
+    assert g.nB <= 64                  # the walk starts at the first list entry
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    c = 1.4426950408889634 / np.sqrt(g.d)
+    b = wl.B - 1
+    r = O.run_head(O.bf16_bits_to_f64(q[b, :, 0]), O.bf16_bits_to_f64(k[b, :, 0]),
+                   O.bf16_bits_to_f64(v[b, :, 0]), wq[0], wk[0], g, perm=perm, meta=meta)
+    growth = 0.0
+    for qb in range(g.nB):
+        kbs = np.nonzero(r["kept"][qb])[0]
+        keys = np.concatenate([np.arange(kb * g.block, kb * g.block + meta[0][kb]) for kb in kbs])
+        qs = r["qr"][qb * g.block: qb * g.block + meta[0][qb]]
+        lg = qs @ r["kr"][keys].T * c
+        first = lg[:, :min(32, meta[0][kbs[0]])].max(axis=1)
+        growth = max(growth, float((lg.max(axis=1) - first).max()))
+    print(f"{name}: largest growth of a row's max after its first stage {growth:.1f} (log2)")
+    assert growth > 16
+    _check_step(wl, q, k, v, wq, wk, list(range(wl.H)), list(range(g.nB)), b=b)
+
+
 def dev_col(col_np):
     return torch.from_numpy(col_np).cuda()
 
