@@ -358,13 +358,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
             int top = diff ? 63 - __clzll(diff) : -1;
             T = top >= 0 ? (kmin & ~((2ull << top) - 1)) : kmin;
             if (top == 63) T = 0;
-            // largest T with count(key >= T) >= need
+            // largest T with count(key >= T) >= need.  Once a candidate
+            // leaves exactly `need` keys at or above it, those are the
+            // kept ones and every later candidate keeps the same set, so
+            // the search stops there (with distinct scores, after the bits
+            // that separate the need-th key from the next).
             for (int bit = top; bit >= 0; --bit) {
                 const uint64_t cand = T | (1ull << bit);
                 int cnt = 0;
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-                if (cnt >= need) T = cand;
+                if (cnt >= need) {
+                    T = cand;
+                    if (cnt == need) break;
+                }
             }
             int gt = 0;
 #pragma unroll
