@@ -477,6 +477,85 @@ def test_sparse_attention_equals_masked_library_sdpa():
     check_sparse_attention_masked_sdpa()
 
 
+def _online_rows(qr, kr, vr, kept, g, valid, rows, rot, lead_empty, c):
+    """The softmax the attention kernel runs, in fp64: stages of 32 keys in a
+    rotated walk of the row's kept blocks, a running max m (log2 units)
+    started at the first stage's max, probabilities 2^(s·c − m) against a
+    stale m, and the lazy rescale decided after the fact: only when one of
+    the stage's two 16-key lane groups sums to 2^8 or more is the stage's max
+    taken, m raised if that max exceeds it by more than 8, and the stage
+    recomputed.  Returns the outputs and the largest accepted probability."""
+    out = np.zeros((len(rows), g.d))
+    pmax = 0.0
+    rescales = 0
+    # lane group of each key of a 32-key stage (the accumulator layout)
+    group = np.array([(k % 8) // 4 for k in range(32)])
+    for i, r in enumerate(rows):
+        qb = r // g.block
+        blocks = list(np.nonzero(kept[qb])[0])
+        blocks = blocks[rot % len(blocks):] + blocks[:rot % len(blocks)]
+        stages = []
+        if lead_empty:
+            stages.append(np.full(32, -np.inf))                   # an empty list entry
+        vstages = [np.zeros((32, g.d))] if lead_empty else []
+        for kb in blocks:
+            for st in range(g.block // 32):
+                k0 = kb * g.block + st * 32
+                n = min(max(valid[kb] - st * 32, 0), 32)
+                s = np.full(32, -np.inf)
+                s[:n] = kr[k0:k0 + n] @ qr[r] * c
+                stages.append(s)
+                vv = np.zeros((32, g.d))
+                vv[:n] = vr[k0:k0 + n]
+                vstages.append(vv)
+        m, l, o = -1e30, 0.0, np.zeros(g.d)
+        if stages[0].max() > m + 8:
+            m = stages[0].max()
+        for s, vv in zip(stages, vstages):
+            # after an empty first entry m is still -1e30: the first stage
+            # with keys overflows to inf, which takes the slow path below
+            with np.errstate(over="ignore"):
+                p = np.exp2(s - m)
+            if max(p[group == 0].sum(), p[group == 1].sum()) >= 256.0:
+                mx = s.max()
+                if mx > m + 8:
+                    al = np.exp2(m - mx)
+                    o *= al
+                    l *= al
+                    m = mx
+                    rescales += 1
+                p = np.exp2(s - m)
+            pmax = max(pmax, p.max())
+            l += p.sum()
+            o += p @ vv
+        out[i] = o / l
+    return out, pmax, rescales
+
+
+def test_online_softmax_with_lazy_rescale_equals_two_pass():
+    """Reading R22 and the after-the-fact rescale: the kernel's online
+    softmax (stale max within 8 log2 units, rescale decided from the lane
+    groups' probability sums) equals the two-pass softmax up to fp64
+    rounding, with every accepted probability at most 2^8, also when logits
+    grow by tens of log2 units along the walk and the walk begins with an
+    empty entry."""
+    g, qr, kr, vr, valid = _attn_case(31, sparsity=0.5, T=4, Hh=8, W=9)
+    qr = qr * 6.0                                   # logits ~ N(0, 36): large growth
+    rng = np.random.default_rng(32)
+    kept = rng.random((g.nB, g.nB)) < 0.6
+    kept[np.arange(g.nB), np.arange(g.nB)] = True
+    ref = O.block_attention(qr, kr, vr, kept, g)
+    rows = _valid_rows(g, valid)[::7]
+    c = 1.0 / math.sqrt(g.d) / math.log(2.0)        # natural logits -> log2 units
+    total = 0
+    for rot, lead in ((0, False), (1, True), (3, False)):
+        out, pmax, rescales = _online_rows(qr, kr, vr, kept, g, valid, rows, rot, lead, c)
+        np.testing.assert_allclose(out, ref[rows], rtol=1e-11, atol=1e-12)
+        assert pmax <= 256.0 * (1 + 1e-12)
+        total += rescales
+    assert total > len(rows)                        # the rescale path really ran
+
+
 def test_attention_bruteforce_loops():
     g, qr, kr, vr, valid = _attn_case(13, sparsity=0.5, T=2, Hh=3, W=3, d=8, block=8)
     assert valid.tolist() == [8, 8, 2]
