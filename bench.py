@@ -55,7 +55,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path shards by head with no exchange, "
-              "and multi-GPU runs are not part of this build", file=sys.stderr)
+              "and runs on more than one GPU are not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

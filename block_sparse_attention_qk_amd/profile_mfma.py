@@ -80,7 +80,7 @@ def main():
     ap.add_argument("--title", default="Matrix-core utilisation and clock per kernel")
     ap.add_argument("--command", default="")
     a = ap.parse_args()
-    lines = [f"# {a.title}", "", "Commands (repository root on the GPU box):", "", "```", a.command, "```", "",
+    lines = [f"# {a.title}", "", "Commands (from the repository root, on the machine with the GPU):", "", "```", a.command, "```", "",
              "clock = GRBM_GUI_ACTIVE / 8 / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / "
              "(GRBM_GUI_ACTIVE / 8) (counters summed over 8 XCDs and 1024 SIMDs).", "",
              "| run | kernel | dispatches | avg ms | clock GHz | MFMA busy |", "|---|---|---|---|---|---|"]

@@ -93,7 +93,7 @@ def summarize(fetch_dir, write_dir, calib_mib, stats_csv=None):
 
 
 def to_markdown(res, title, command):
-    lines = [f"# {title}", "", "Commands (repository root on the GPU box):", "", "```", command, "```", "",
+    lines = [f"# {title}", "", "Commands (from the repository root, on the machine with the GPU):", "", "```", command, "```", "",
              f"Calibration: one {res['calib_mib']} MiB device copy; FETCH_SIZE scaled by "
              f"{res['fetch_scale']:.3f}, WRITE_SIZE by {res['write_scale']:.3f} (known bytes / counted bytes).",
              "", "| kernel | read GB | written GB | total GB | avg ms | GB/s |", "|---|---|---|---|---|---|"]
