@@ -264,7 +264,13 @@ class Plan:
 
 
 def sva_plan_create(B, H, T, Hh, W, d, block, sparsity, dense_flag=0) -> Plan:
-    return sva_plan_create_ex(sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, dense_flag))
+    h = ctypes.c_void_p()
+    _check(lib().sva_plan_create(ctypes.byref(h), B, H, T, Hh, W, d, block, float(sparsity),
+                                 dense_flag))
+    info = sva_plan_info()
+    _check(lib().sva_plan_get_info(h, ctypes.byref(info)))
+    # the description with the same defaults (host only), for the shape helpers
+    return Plan(h, sva_plan_desc_init(B, H, T, Hh, W, d, block, sparsity, dense_flag), info)
 
 
 def sva_plan_create_ex(desc: sva_plan_desc) -> Plan:

@@ -242,6 +242,28 @@ def test_attention_parity(name):
     assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
 
 
+def test_plain_create_equals_create_ex():
+    """sva_plan_create (positional arguments; default tile, RoPE split, theta
+    and eps) makes the plan sva_plan_create_ex makes from the default
+    description, and a step run with it is bit-identical."""
+    wl = I.WORKLOADS["tiny"]
+    assert wl.tile == (4, 4, 4) and wl.rope_split == (0, 0, 0)   # the defaults
+    plain = S.sva_plan_create(wl.B, wl.H, wl.T, wl.Hh, wl.W, wl.d, wl.block, wl.sparsity,
+                              wl.flags)
+    run = GpuRun(wl, *workload_inputs(wl))
+    for f, _ in S.sva_plan_info._fields_:
+        a, b = getattr(plain.info, f), getattr(run.plan.info, f)
+        if not isinstance(a, (int, float)):
+            a, b = list(a), list(b)
+        assert a == b, f
+    buf = S.Buffers(plain)
+    S.forward(plain, run.q, run.k, run.v, run.wq, run.wk, buf)
+    ref = run.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(buf.o.view(torch.int16), ref.o.view(torch.int16))
+    S.sva_destroy(plain)
+
+
 # 80 blocks of 64 tokens: query blocks from 64 on start their walk at the
 # first list entry at or after block 64
 OOB = I.custom("oob80", 1, 2, 5, 32, 32, 64, 64, 0.5, tile=(1, 4, 16), seed_base=10600)
