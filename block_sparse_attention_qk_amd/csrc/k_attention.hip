@@ -25,9 +25,9 @@
 //   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries; the
 //                    operand of lane l for channel step s is the 16 bytes at
 //                    (s·64 + l)·16 of the K stage
-//   softmax on S^T   each lane owns one query column: row max and sums are
-//                    lane-local plus one exchange between the two lane
-//                    halves (v_permlane32_swap)
+//   softmax on S^T   each lane owns one query column: sums are lane-local;
+//                    a row max, when one is needed, is lane-local plus one
+//                    exchange between the two lane halves (v_permlane32_swap)
 //   O^T += V^T · P^T v_mfma_f32_32x32x16_bf16, M = channels, N = queries;
 //                    P^T comes straight from the S^T accumulators; the V
 //                    stage holds four chunks of 8 keys, each chunk as d rows
@@ -41,7 +41,10 @@
 // The running max is raised only when a row's new max exceeds it by more
 // than 8 (log2 units); in between, probabilities are taken against the
 // stale max (at most 2^8, exact in the final division), which skips most
-// rescales of the accumulator.
+// rescales of the accumulator.  The row's first stage sets the max; later
+// stages are exponentiated against it first, and only a wave in which some
+// lane's 16 probabilities sum to 2^8 or more takes the stage max and
+// applies the rule, so the common stage needs no max at all.
 //
 // Roofline: 4·BLK²·d flops per (query block, key block) pair on the MFMA
 // pipe (8.4 MFLOP at BLK = d = 128) against 2·BLK·d·2 bytes of K and V
