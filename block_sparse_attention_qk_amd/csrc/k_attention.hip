@@ -131,10 +131,10 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
         : "memory", "m0");
 }
 // The same copy from a wave-uniform base pointer (SGPRs) and this lane's
-// byte offset; the LDS destination is a wave-uniform base plus a constant,
-// added into M0 in the same block (the add is the wait state the load needs
-// after the M0 write is not: one s_nop remains).
-// `imm` must fold to a constant once the caller's loops are unrolled.
+// byte offset.  The LDS destination is a wave-uniform base plus a constant,
+// added into M0 in the same block; the load still needs one wait state
+// after that M0 write (the s_nop).  `imm` must fold to a constant once the
+// caller's loops are unrolled.
 __device__ __forceinline__ void lds_dma16_at(const void* base, uint32_t lane_off,
                                              uint32_t lds_base, uint32_t imm) {
     asm volatile(
