@@ -6,6 +6,8 @@ No compute call runs here (no GPU)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -127,3 +129,22 @@ def test_partial_rope_split_accepted():
     desc = S.sva_plan_desc_init(1, 2, 4, 8, 8, 128, 128, 0.5, rope_split=(32, 32, 32))
     info = S.sva_plan_query(desc)
     assert list(info.rope_split) == [32, 32, 32]
+
+
+def test_c_program_host_calls(tmp_path):
+    """The header compiles as C99 and the library links from C: a plain C
+    program (tests/c_abi_host.c) runs the host-only calls and checks the
+    tile order, budget, row offsets and error codes written out by hand."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    S.lib()                                   # the library must be built
+    libdir = os.path.dirname(S.LIB_PATH)
+    exe = str(tmp_path / "c_abi_host")
+    subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_host.c"),
+                    "-L", libdir, "-lsva", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok"
