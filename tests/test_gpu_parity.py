@@ -16,6 +16,10 @@ checked on sampled heads and query blocks (the launch configuration is the
 one the benchmark times).
 """
 
+import os
+import shutil
+import subprocess
+
 import numpy as np
 import pytest
 import torch
@@ -262,6 +266,56 @@ def test_plain_create_equals_create_ex():
     torch.cuda.synchronize()
     assert torch.equal(buf.o.view(torch.int16), ref.o.view(torch.int16))
     S.sva_destroy(plain)
+
+
+_C_STEP = {"tiny": I.WORKLOADS["tiny"],
+           "c128": I.custom("c128", 1, 2, 3, 13, 17, 128, 128, 0.6, flags=I.KEEP_SAME_FRAME,
+                            tile=(2, 8, 8), seed_base=10800)}
+
+
+@pytest.fixture(scope="module")
+def c_step_exe(tmp_path_factory):
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(S.LIB_PATH)
+    exe = str(tmp_path_factory.mktemp("c_step") / "c_abi_step")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi_step.c"), "-L", libdir, "-lsva",
+                    "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath," + libdir,
+                    "-Wl,-rpath,/opt/rocm/lib", "-o", exe], check=True)
+    return exe
+
+
+@pytest.mark.parametrize("name", list(_C_STEP))
+def test_c_program_step(name, c_step_exe, tmp_path):
+    """A plain C caller (tests/c_abi_step.c: hipMalloc'd buffers, the fused
+    calls on the default stream) gets the same raster output as the Python
+    binding's forward(), bit for bit; both use the default tile."""
+    wl = _C_STEP[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    src = tmp_path / "in.bin"
+    dst = tmp_path / "out.bin"
+    with open(src, "wb") as f:
+        for a in (q, k, v):
+            f.write(np.ascontiguousarray(a, np.uint16).tobytes())
+        for a in (wq, wk):
+            f.write(np.ascontiguousarray(a, np.float32).tobytes())
+    print(f"{name}: running the C program", flush=True)
+    r = subprocess.run([c_step_exe, str(wl.B), str(wl.H), str(wl.T), str(wl.Hh), str(wl.W),
+                        str(wl.d), str(wl.block), repr(wl.sparsity), str(wl.flags), str(src),
+                        str(dst)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    out_c = np.fromfile(dst, dtype=np.uint16).reshape(q.shape)
+    plan = S.sva_plan_create(wl.B, wl.H, wl.T, wl.Hh, wl.W, wl.d, wl.block, wl.sparsity, wl.flags)
+    buf = S.Buffers(plan)
+    S.forward(plan, dev(q), dev(k), dev(v), torch.from_numpy(wq).cuda(),
+              torch.from_numpy(wk).cuda(), buf)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(buf.o), out_c)
+    S.sva_destroy(plan)
 
 
 # 80 blocks of 64 tokens: query blocks from 64 on start their walk at the
