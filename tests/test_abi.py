@@ -148,3 +148,24 @@ def test_c_program_host_calls(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "ok"
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: with the library absent the binding raises before any
+    call runs."""
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "libsva.so"))
+    monkeypatch.setattr(S, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        S.lib()
+    with pytest.raises(RuntimeError):
+        S.sva_plan_query(S.sva_plan_desc())
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus N > 1 exits with status 2 and a
+    message, before it touches a device."""
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
