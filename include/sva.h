@@ -2,7 +2,7 @@
  * sva.h — block-sparse video self-attention on MI355X (gfx950).
  *
  * One attention call of a video diffusion transformer over T×Hh×W latent
- * tokens (plus optional extra audio/text tokens), in five steps:
+ * tokens (plus optional extra audio/text tokens), in four calls:
  *
  *   sva_qk_norm_rope   QK-RMSNorm + 3D-RoPE on Q and K, fused in one kernel
  *   sva_reorder        raster tokens -> 3D-tile order (and back for O)
