@@ -442,14 +442,6 @@ def select_from_scores(scores, geom: Geometry, meta=None):
     return kept, scores, thresh, smax
 
 
-def kept_to_csr(kept):
-    """Row pointer and ascending column list of a kept mask."""
-    lens = kept.sum(axis=1)
-    row_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    cols = np.nonzero(kept)[1].astype(np.int64)   # row-major → ascending per row
-    return row_ptr, cols
-
-
 # --------------------------------------------------------------------------
 # Step 5: attention over the kept blocks
 # --------------------------------------------------------------------------
@@ -502,19 +494,6 @@ def block_attention(qr, kr, vr, kept, geom: Geometry, meta=None, qblocks=None):
         e = np.exp(logits - m)
         out[qb * b: qb * b + valid[qb]] = (e @ vals) / e.sum(axis=1, keepdims=True)
     return out
-
-
-def attention_probabilities(qr, kr, kept, geom: Geometry, qb, meta=None):
-    """Softmax weights of the valid queries of block qb over the valid keys
-    of its kept blocks (for row-sum checks): returns (P, key indices)."""
-    valid, _, _, _ = block_meta(geom) if meta is None else meta
-    b, d = geom.block, geom.d
-    keys = np.concatenate([np.arange(kb * b, kb * b + valid[kb])
-                           for kb in np.nonzero(kept[qb])[0]])
-    qs = np.asarray(qr, np.float64)[qb * b: qb * b + valid[qb]]
-    logits = (qs @ np.asarray(kr, np.float64)[keys].T) / math.sqrt(d)
-    e = np.exp(logits - logits.max(axis=1, keepdims=True))
-    return e / e.sum(axis=1, keepdims=True), keys
 
 
 # --------------------------------------------------------------------------

@@ -641,13 +641,58 @@ def test_compensation_brute_force():
             np.testing.assert_allclose(got[p], num / den, rtol=1e-10, atol=1e-12)
 
 
-def test_attention_row_sums_are_one():
-    g, qr, kr, vr, valid = _attn_case(14, sparsity=0.5)
-    kept = np.eye(g.nB, dtype=bool) | (np.arange(g.nB)[None, :] == 0)
+def check_attention_row_sums(flags=0, sparsity=0.5):
+    """Row sums of the softmax weights equal 1, read off block_attention
+    itself: with V set to the identity (d = Np, one value channel per key
+    position) the output row of query p is its weight vector over the key
+    positions.  Every valid row's weights are non-negative and sum to 1;
+    without compensation they vanish outside the row's kept blocks and on
+    padding keys; with compensation a dropped block's weight is spread
+    evenly (its mean value) over its valid keys.  With V = 1 on the valid
+    keys the output is 1 on every valid row."""
+    g = O.Geometry(B=1, H=1, T=2, Hh=4, W=6, d=64, block=16, sparsity=sparsity, tile=(1, 4, 4),
+                   flags=flags, n_extra=16)
+    assert g.Np == g.d
+    valid, _, _, _ = O.block_meta(g)
+    rng = np.random.default_rng(14 + flags)
+    qr, kr = (rng.standard_normal((g.Np, g.d)) * 2.0 for _ in range(2))
+    rows = _valid_rows(g, valid)
+    pad = np.setdiff1d(np.arange(g.Np), rows)
+    qr[pad] = kr[pad] = 0.0
+    kept = rng.random((g.nB, g.nB)) < 0.4
+    kept[np.arange(g.nB), np.arange(g.nB)] = True
+    if g.dense:
+        kept[:] = True
+    eye = np.eye(g.Np)
+    eye[pad] = 0.0
+    P = O.block_attention(qr, kr, eye, kept, g)
+    np.testing.assert_allclose(P[rows].sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    assert np.all(P >= 0)
+    assert np.all(P[:, pad] == 0) and np.all(P[pad] == 0)
+    comp = bool(flags & O.SVA_COMPENSATE)
     for qb in range(g.nB):
-        P, _ = O.attention_probabilities(qr, kr, kept, g, qb)
-        np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=1e-14)
-        assert np.all(P >= 0)
+        r = slice(qb * g.block, qb * g.block + valid[qb])
+        for kb in range(g.nB):
+            c = slice(kb * g.block, kb * g.block + valid[kb])
+            if kept[qb, kb]:
+                assert np.all(P[r, c] > 0)
+            elif comp:
+                w = P[r, c]
+                np.testing.assert_allclose(w, np.repeat(w[:, :1], w.shape[1], axis=1), rtol=1e-12)
+                assert np.all(w > 0)
+            else:
+                assert np.all(P[r, c] == 0)
+    ones = np.zeros((g.Np, g.d))
+    ones[rows] = 1.0
+    o1 = O.block_attention(qr, kr, ones, kept, g)
+    np.testing.assert_allclose(o1[rows], 1.0, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("flags,sparsity", [(0, 0.5), (0, 0.0), (O.SVA_DENSE, 0.7),
+                                            (O.SVA_COMPENSATE, 0.5),
+                                            (O.SVA_COMPENSATE | O.SVA_KEEP_SAME_FRAME, 0.6)])
+def test_attention_row_sums_are_one(flags, sparsity):
+    check_attention_row_sums(flags, sparsity)
 
 
 def test_attention_permutation_equivariance():
@@ -800,3 +845,45 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "subblock_scores", bad_sub)
     assert _fails(check_subblock_exact)
     monkeypatch.setattr(O, "subblock_scores", orig_sub)
+    # 12. compensation whose softmax denominator leaves the dropped blocks out
+    #     (their weighted mean values added to the numerator only)
+    def bad_den(qr, kr, vr, kept, g, meta=None, qblocks=None):
+        if not (g.flags & O.SVA_COMPENSATE):
+            return orig_attn2(qr, kr, vr, kept, g, meta, qblocks)
+        valid = O.block_meta(g)[0]
+        b, out = g.block, np.zeros((g.Np, g.d))
+        for qb in range(g.nB):
+            keys = np.concatenate([np.arange(kb * b, kb * b + valid[kb])
+                                   for kb in np.nonzero(kept[qb])[0]])
+            qs = np.asarray(qr)[qb * b: qb * b + valid[qb]]
+            lg = qs @ np.asarray(kr)[keys].T / math.sqrt(g.d)
+            m = lg.max(axis=1, keepdims=True)
+            e = np.exp(lg - m)
+            num = e @ np.asarray(vr)[keys]
+            for kb in np.nonzero(~kept[qb])[0]:
+                km = np.asarray(kr)[kb * b: kb * b + valid[kb]].mean(axis=0)
+                vm = np.asarray(vr)[kb * b: kb * b + valid[kb]].mean(axis=0)
+                wgt = valid[kb] * np.exp((qs @ km)[:, None] / math.sqrt(g.d) - m)
+                num = num + wgt * vm[None, :]
+            out[qb * b: qb * b + valid[qb]] = num / e.sum(axis=1, keepdims=True)
+        return out
+    monkeypatch.setattr(O, "block_attention", bad_den)
+    assert _fails(lambda: check_attention_row_sums(O.SVA_COMPENSATE, 0.5))
+    monkeypatch.setattr(O, "block_attention", orig_attn2)
+    # 13. sparse attention whose softmax denominator runs over the valid keys
+    #     of every block, kept or not (numerator over the kept ones only)
+    def bad_den2(qr, kr, vr, kept, g, meta=None, qblocks=None):
+        valid = O.block_meta(g)[0]
+        b, out = g.block, np.zeros((g.Np, g.d))
+        allk = np.concatenate([np.arange(kb * b, kb * b + valid[kb]) for kb in range(g.nB)])
+        for qb in range(g.nB):
+            qs = np.asarray(qr)[qb * b: qb * b + valid[qb]]
+            lg = qs @ np.asarray(kr)[allk].T / math.sqrt(g.d)
+            e = np.exp(lg - lg.max(axis=1, keepdims=True))
+            on = kept[qb][allk // b]
+            out[qb * b: qb * b + valid[qb]] = ((e * on) @ np.asarray(vr)[allk]
+                                                / e.sum(axis=1, keepdims=True))
+        return out
+    monkeypatch.setattr(O, "block_attention", bad_den2)
+    assert _fails(lambda: check_attention_row_sums(0, 0.5))
+    monkeypatch.setattr(O, "block_attention", orig_attn2)
