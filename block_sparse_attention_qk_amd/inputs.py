@@ -93,6 +93,18 @@ WORKLOADS = {
     "wan720p_subblock": Workload("wan720p_subblock", 1, 40, 21, 45, 80, 128, 128, 0.75,
                                  flags=KEEP_SAME_FRAME, tile=(2, 8, 8), temperature=True,
                                  seed_base=2000, scorer=1, budget_multiple=8),
+    # the SubBlock router at the configuration that defines it: 64-token
+    # blocks cut into four 16-token sub-blocks, budget rounded up to a
+    # multiple of 8 blocks, on the 480p inputs at sparsity 0.75
+    "wan480p_subblock": Workload("wan480p_subblock", 1, 12, 21, 30, 52, 128, 64, 0.75,
+                                 tile=(3, 4, 8), seed_base=1000, scorer=1, subblocks=4,
+                                 budget_multiple=8),
+    # the per-rank prologue shape of the packed video + audio benchmark:
+    # 4,722 rows (= 2·3·787, so the grid is 2×3×787: the pages give rows,
+    # not a grid, and the prologue's work per row does not depend on it),
+    # 56 heads of 128 channels, RoPE over 96 of them (32 per axis)
+    "h3_prologue": Workload("h3_prologue", 1, 56, 2, 3, 787, 128, 128, 0.0,
+                            seed_base=7000, rope_split=(32, 32, 32)),
     # size limits: 4096 blocks per head (the plan's maximum; 262,144 tokens in
     # 64-token blocks), and 1538 blocks (1536 video + 2 of extra tokens, whose
     # rows and columns are always kept)

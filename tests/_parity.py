@@ -134,6 +134,56 @@ def compare_masks(gpu_kept, ref_kept, scores, thresh, smax, forced):
     return n, int(ok.sum())
 
 
+def oracle_selection(qr_f, kr_f, g, meta):
+    """The oracle's ranking of tile-ordered Q', K' (float64 values) under
+    the geometry's scorer: (kept, scores, thresh, smax)."""
+    if g.scorer == O.SCORER_SUBBLOCK:
+        sc = O.subblock_scores(O.subblock_means(qr_f, g, meta[0]),
+                               O.subblock_means(kr_f, g, meta[0]), g, meta[0])
+        return O.select_from_scores(sc, g, meta)
+    return O.select_blocks(O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]),
+                           g, meta)
+
+
+def chain_flips(gpu_kept, stage, chain, forced):
+    """Classify the differences between the GPU's mask and the chained
+    oracle's mask of one head.
+
+    The GPU ranks its own Q', K'; the chained oracle ranks the output of
+    its own float64 prologue, which can differ from the GPU's by a bf16
+    rounding step here and there, and so can move scores.  ``stage`` is the
+    oracle's ranking of the GPU's own Q', K' (kept, scores, thresh, smax),
+    ``chain`` the chained oracle's (dict with kept, scores, smax).  A flip
+    on (qb, kb) is explained when
+      - kb is not forced for qb,
+      - the GPU agrees with the oracle's ranking of the GPU's own inputs at
+        (qb, kb), or differs from it only by an excused boundary tie, and
+      - the chained score gap of kb to the other side of the row's cut is
+        at most twice the largest score change between the two oracle
+        rankings of that row (the change the rounding differences made)
+        plus the tie margin.
+    Returns a list of (qb, kb, relative gap, relative shift, explained),
+    relative to the chained row's largest |score|."""
+    skept, sscores, sthresh, ssmax = stage
+    ck, cs, csmax = chain["kept"], chain["scores"], chain["smax"]
+    out = []
+    for qb, kb in zip(*np.nonzero(gpu_kept != ck)):
+        free = ~forced[qb]
+        if ck[qb, kb]:
+            others = cs[qb, free & ~ck[qb]]
+            gap = cs[qb, kb] - (others.max() if others.size else -np.inf)
+        else:
+            others = cs[qb, free & ck[qb]]
+            gap = (others.min() if others.size else np.inf) - cs[qb, kb]
+        shift = float(np.abs(sscores[qb] - cs[qb])[free].max()) if free.any() else 0.0
+        agrees = gpu_kept[qb, kb] == skept[qb, kb] or (
+            abs(sscores[qb, kb] - sthresh[qb]) <= TIE_MARGIN * ssmax[qb])
+        scale = max(float(csmax[qb]), 1e-300)
+        ok = bool(not forced[qb, kb] and agrees and gap <= 2.0 * shift + TIE_MARGIN * scale)
+        out.append((int(qb), int(kb), float(gap) / scale, shift / scale, ok))
+    return out
+
+
 class GpuRun:
     """The whole step on the GPU with every intermediate kept."""
 

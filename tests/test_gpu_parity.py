@@ -27,8 +27,9 @@ import torch
 import block_sparse_attention_qk_amd as S
 from block_sparse_attention_qk_amd import inputs as I
 import oracle.sva_oracle as O
-from _parity import (MAX_ABS, REL_L2, GpuRun, compare_masks, dev, geometry, host, host_f64,
-                     kept_from_col, max_abs, prologue_check, rel_l2, workload_inputs)
+from _parity import (MAX_ABS, REL_L2, GpuRun, chain_flips, compare_masks, dev, geometry, host,
+                     host_f64, kept_from_col, max_abs, oracle_selection, prologue_check, rel_l2,
+                     workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +58,15 @@ SMALL = {
     # SubBlock scorer, 64-token blocks in 2 runs, ragged tail, extra tokens
     "sub64": I.custom("sub64", 2, 2, 3, 10, 14, 64, 64, 0.5, tile=(2, 4, 8), n_extra=64,
                       seed_base=9900, scorer=1, subblocks=2),
+    # SubBlock router as the pages define it: 64-token blocks cut into four
+    # 16-token sub-blocks, budget in units of 8 blocks; d = 128, a ragged
+    # last block (4 valid tokens: one partial run, three empty), extra
+    # tokens (one always-kept column beside 7 ranked blocks per row)
+    "sub64x4": I.custom("sub64x4", 1, 2, 5, 14, 22, 128, 64, 0.75, tile=(4, 4, 4), n_extra=64,
+                        seed_base=11000, scorer=1, subblocks=4, budget_multiple=8),
+    # the same router at d = 64 with B = 2 and 32-token budget rounding off
+    "sub64x4_d64": I.custom("sub64x4_d64", 2, 2, 4, 12, 18, 64, 64, 0.6, tile=(2, 4, 8),
+                            seed_base=11100, scorer=1, subblocks=4),
     # compensation of the dropped blocks: ragged 128-token blocks with extra
     # tokens and same-frame forcing; 64-token blocks, B = 2
     "comp128": I.custom("comp128", 1, 2, 5, 13, 17, 128, 128, 0.6,
@@ -536,17 +546,29 @@ def test_chained_parity(name):
     for (b, h), r in ref.items():
         worst_rel = max(worst_rel, rel_l2(out[b, :, h], r["o"]))
         worst_abs = max(worst_abs, max_abs(out[b, :, h], r["o"]))
-    diffs = 0
+    flips = []
     if not run.plan.info.dense:
         col = run.buf.col.cpu().numpy()
         _, row_ptr, _ = run.plan.host_tables()
         nnz = int(run.plan.info.nnz_per_head)
+        forced, _ = O.forced_blocks(g, meta)
         for (b, h), r in ref.items():
             bh = b * wl.H + h
             kept = kept_from_col(col[bh * nnz:(bh + 1) * nnz], row_ptr, g.nB)
-            diffs += int((kept != r["kept"]).sum())
-    print(f"{name}: chained rel_l2 {worst_rel:.2e} max_abs {worst_abs:.2e} mask diffs {diffs}")
+            if np.array_equal(kept, r["kept"]):
+                continue
+            # the oracle's ranking of the GPU's own Q', K' explains each flip
+            want = np.zeros((g.Np, g.d), np.uint16)
+            want[perm] = host(run.buf.qn[b, :, h])
+            qr_f = O.bf16_bits_to_f64(want)
+            want[perm] = host(run.buf.kn[b, :, h])
+            kr_f = O.bf16_bits_to_f64(want)
+            stage = oracle_selection(qr_f, kr_f, g, meta)
+            flips += [((b, h),) + f for f in chain_flips(kept, stage, r, forced)]
+    print(f"{name}: chained rel_l2 {worst_rel:.2e} max_abs {worst_abs:.2e} "
+          f"mask flips {len(flips)} {flips}")
     assert worst_rel <= REL_L2 and worst_abs <= MAX_ABS
+    assert all(f[-1] for f in flips), flips
     # the fused step computes the same bits
     fb = run.run_fused()
     assert np.array_equal(host(fb.o), host(run.buf.o))
@@ -624,8 +646,8 @@ def test_binding_rejects_bad_tensors():
 # ------------------------------------------------------------------ full-size workloads
 
 FULL = ["wan480p_dense", "wan480p_sp75", "wan720p_sp75", "hunyuan720p_sp80",
-        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock", "hunyuan720p_comp",
-        "max4096", "blocks1538"]
+        "hunyuan720p_dense", "packed768p_sp80", "wan720p_subblock", "wan480p_subblock",
+        "hunyuan720p_comp", "max4096", "blocks1538"]
 _full_cache = {}
 
 
@@ -653,6 +675,7 @@ def _check_step(wl, q, k, v, wq, wk, heads, qbs, b=0):
     nnz = int(run.plan.info.nnz_per_head)
     col = run.buf.col.cpu().numpy() if run.buf.col is not None else None
     stats = dict(ulp_mism=0, elems=0, mask_diffs=0, mask_excused=0, chain_mask_diffs=0)
+    flips = []     # (head, qb, kb, relative gap, relative score shift, explained)
     fails = []
     worst = dict(att_rel=0.0, att_abs=0.0, ch_rel=0.0, ch_abs=0.0)
     for h in heads:
@@ -690,13 +713,8 @@ def _check_step(wl, q, k, v, wq, wk, heads, qbs, b=0):
         qr_f = O.bf16_bits_to_f64(qr_g)
         kr_f = O.bf16_bits_to_f64(kr_g)
         if col is not None:
-            if g.scorer == O.SCORER_SUBBLOCK:
-                sc_ref = O.subblock_scores(O.subblock_means(qr_f, g, meta[0]),
-                                           O.subblock_means(kr_f, g, meta[0]), g, meta[0])
-                kept_ref, scores, thresh, smax = O.select_from_scores(sc_ref, g, meta)
-            else:
-                kept_ref, scores, thresh, smax = O.select_blocks(
-                    O.pool_means(qr_f, g, meta[0]), O.pool_means(kr_f, g, meta[0]), g, meta)
+            stage = oracle_selection(qr_f, kr_f, g, meta)
+            kept_ref, scores, thresh, smax = stage
             kept_g = kept_from_col(col[(b * wl.H + h) * nnz:(b * wl.H + h + 1) * nnz], row_ptr, g.nB)
             n, e = compare_masks(kept_g, kept_ref, scores, thresh, smax, forced)
             stats["mask_diffs"] += n
@@ -715,7 +733,10 @@ def _check_step(wl, q, k, v, wq, wk, heads, qbs, b=0):
             fails.append(("reorder inverse", h))
         # chained: the oracle from the raw inputs
         r = O.run_head(qh, kh, vh, wq[h], wk[h], g, qblocks=qbs, perm=perm, meta=meta)
-        stats["chain_mask_diffs"] += int((r["kept"] != kept_g).sum())
+        if col is not None:
+            fl = chain_flips(kept_g, stage, r, forced)
+            stats["chain_mask_diffs"] += len(fl)
+            flips += [(h,) + f for f in fl]
         worst["ch_rel"] = max(worst["ch_rel"], rel_l2(o_g[rows], r["o_r"][rows]))
         worst["ch_abs"] = max(worst["ch_abs"], max_abs(o_g[rows], r["o_r"][rows]))
     fb = run.run_fused()
@@ -723,7 +744,11 @@ def _check_step(wl, q, k, v, wq, wk, heads, qbs, b=0):
         fails.append(("fused step differs from the staged step",))
     del fb
     print(f"{name}: heads {heads} qblocks {qbs} {stats} {worst}", flush=True)
+    if flips:
+        print(f"{name}: chained mask flips (head, qb, kb, gap/max|s|, shift/max|s|, explained): "
+              f"{flips}; largest gap {max(f[3] for f in flips):.2e}", flush=True)
     assert not fails, fails
+    assert all(f[-1] for f in flips), flips
     assert stats["ulp_mism"] <= 1e-3 * stats["elems"]
     assert stats["mask_diffs"] == stats["mask_excused"]
     assert worst["att_rel"] <= REL_L2 and worst["att_abs"] <= MAX_ABS
