@@ -5,8 +5,8 @@
         --calib-mib 1024 [--stats KERNEL_STATS_CSV] --out-json F.json --out-md F.md
 
 Both runs profile ``bench.py --calib-copy-mib N``, which does one plain
-device-to-device copy of N MiB (a blit kernel that reads and writes exactly
-N MiB) next to the step's kernels.  rocprofv3 reports ``FETCH_SIZE`` and
+device-to-device copy of N MiB (the library's streaming copy kernel, which
+reads and writes exactly N MiB) next to the step's kernels.  rocprofv3 reports ``FETCH_SIZE`` and
 ``WRITE_SIZE`` in KiB per dispatch; the counters need not count every byte
 (the read counter sees about half of a copy's reads on this part), so each
 is scaled by known bytes / counted bytes of that copy.  The result is the
@@ -57,8 +57,14 @@ def _counter_rows(run_dir: str, counter: str):
     return per
 
 
+def _is_copy(name: str) -> bool:
+    """The calibration copy: the library's streaming copy kernel (or the
+    runtime's blit kernel in older runs)."""
+    return "stream_copy_kernel" in name or "copyBuffer" in name
+
+
 def _calibration(per: dict, calib_bytes: float) -> float:
-    copies = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+    copies = [v for k, vs in per.items() if _is_copy(k) for v in vs]
     if not copies:
         raise ValueError("no copy kernel in the counter run (run bench.py with --calib-copy-mib)")
     counted = max(copies) * 1024.0
@@ -78,7 +84,7 @@ def summarize(fetch_dir, write_dir, calib_mib, stats_csv=None):
                 dur[_short(r["Name"])] = float(r["AverageNs"]) * 1e-9
     kernels = {}
     for k in sorted(set(fetch) | set(write)):
-        if "copyBuffer" in k:
+        if _is_copy(k):
             continue
         fb = (sum(fetch.get(k, [0])) / max(1, len(fetch.get(k, [0])))) * 1024.0 * f_fac
         wb = (sum(write.get(k, [0])) / max(1, len(write.get(k, [0])))) * 1024.0 * w_fac

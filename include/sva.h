@@ -276,6 +276,17 @@ int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void
                      const int32_t* col, const void* km_t, const void* vm_t, void* o,
                      int o_layout, void* stream);
 
+/* ---- measurement ---- */
+
+/* Plain device-to-device copy of `bytes` bytes (dst, src: device memory,
+ * 16-byte aligned, not overlapping), enqueued on `stream`.  It is the
+ * reference the HBM-bound kernels of the step are measured against: the
+ * read + write rate a streaming kernel reaches on this part (16-byte
+ * accesses, four per thread in flight, non-temporal hints), and a kernel
+ * whose byte count is known, so profiler byte counters can be scaled by
+ * it.  Not part of the attention step. */
+int sva_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* ---- errors ---- */
 const char* sva_status_string(int status);
 const char* sva_last_error(void);
