@@ -154,9 +154,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left unconstrained.
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
-// Stage buffers of K and of V (32·d bf16 each).  K of stage st+1 is read in
-// iteration st and V of stage st in iteration st, so with copies at least
-// one iteration ahead K needs three buffers and V two.  With 128-token
+// Stage buffers of K and of V (32·d bf16 each).  K of stage st+1 and V of
+// stage st-1 are read in iteration st, so with K copies at least one
+// iteration ahead of their use K needs three buffers, and V two (a stage's
+// V copied in its own iteration, read in the next).  With 128-token
 // blocks: four of each (copies up to three stages ahead; two workgroups of
 // four waves fill a CU's registers).  With 64-token blocks a workgroup has
 // only two waves: three K and two V buffers (40 KB at d = 128) let four
@@ -196,7 +197,7 @@ void attn_kernel(AttnArgs a) {
     static_assert(NU % SPB == 0, "a loop body covers whole blocks");
     // list entries a loop body touches (its stages and the copies it issues)
     constexpr int NE = (NU + NBK - 2) / SPB + 1;
-    // At the end of iteration st, K of stage st+2 and V of stage st+1 must
+    // At the end of iteration st, K of stage st+2 and V of stage st must
     // have landed; they were issued in iterations st+3-NBK and st+2-NBV, so
     // the copies of the min(NBK-3, NBV-2) latest iterations may stay in flight.
     constexpr int kInFlight = (NBK - 3 < NBV - 2 ? NBK - 3 : NBV - 2) * 2 * LPW;
@@ -464,18 +465,21 @@ void attn_kernel(AttnArgs a) {
     } while (0)
 
     // Software pipeline, one wave: iteration st computes S^T of stage st+1
-    // while it turns S^T of stage st into probabilities, then O^T += V^T P^T
-    // of stage st while it takes the max of stage st+1.  The matrix
-    // instructions of one half have no dependence on the vector
-    // instructions beside them, so one wave keeps both pipes busy.
-    // K copies run NBK-1 and V copies NBV-1 stages ahead; at the end of
-    // iteration st, K of stage st+2 and V of stage st+1 (both read in
-    // iteration st+1) have landed.  The loop has no ordinary LDS stores, only copies: after this
-    // wave's wait, a bare s_barrier makes every wave's part visible and
-    // orders every wave's reads of the oldest buffers before the copies
-    // into them.  (__syncthreads() would add a workgroup release fence,
-    // which waits for every outstanding load, the copies still ahead
-    // included.)
+    // and O^T += V^T P^T of stage st-1 (16 matrix instructions) while it
+    // turns S^T of stage st into probabilities; none of the three depends
+    // on another, so the vector work spreads over all 16 matrix
+    // instructions.  (A rescale of the accumulators in iteration st comes
+    // after the product of stage st-1 in program order, which was taken
+    // against the old max.)  The first iteration's product reads a zeroed
+    // V buffer with P = 0; the last stage's product follows the loop.
+    // K copies run NBK-1 and V copies NBV-2 stages ahead; at the end of
+    // iteration st, K of stage st+2 and V of stage st (both read in
+    // iteration st+1) have landed.  The loop has no ordinary LDS stores,
+    // only copies: after this wave's wait, a bare s_barrier makes every
+    // wave's part visible and orders every wave's reads of the oldest
+    // buffers before the copies into them.  (__syncthreads() would add a
+    // workgroup release fence, which waits for every outstanding load, the
+    // copies still ahead included.)
     f32x16_t sc, sn;
     float mx;
     bf16x8_t pb[2];
@@ -494,9 +498,13 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < NBK - 1; ++u) SVA_COPY_K(kb8 + E[u / SPB].off, u % SPB, u);
 #pragma unroll
-        for (int u = 0; u < NBV - 1; ++u) SVA_COPY_V(vb8 + E[u / SPB].off, u % SPB, u);
+        for (int u = 0; u < NBV - 2; ++u) SVA_COPY_V(vb8 + E[u / SPB].off, u % SPB, u);
+        // the V buffer the first iteration's product reads (with P = 0)
+        for (int i = tid; i < CPS; i += NT) sV[NBV - 1][i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pb[s2] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __builtin_amdgcn_s_barrier();
+        __syncthreads();
         SVA_SCORE(sK[0], sc);
         SVA_MAX(sc, mx);
         SVA_MASK(E[0].nv, sc, mx);
@@ -517,21 +525,23 @@ void attn_kernel(AttnArgs a) {
         for (int u = 0; u < NU; ++u) {
             // a body's later entries may lie past the end of the row
             if (u > 0 && u % SPB == 0 && w + u / SPB >= len) break;
-            const int ck = u + NBK - 1, cv = u + NBV - 1, cs = u + 1;
+            const int ck = u + NBK - 1, cv = u + NBV - 2, cs = u + 1;
             SVA_COPY_K(kb8 + E[ck / SPB].off, ck % SPB, ck % NBK);
             SVA_COPY_V(vb8 + E[cv / SPB].off, cv % SPB, cv % NBV);
             const int lim = E[cs / SPB].nv - (cs % SPB) * SK;
             // one straight-line region: the scheduler interleaves the
-            // matrix and vector halves
+            // matrix instructions and the vector work
             SVA_SCORE(sK[cs % NBK], sn);
+            SVA_PV(sV[(u + NBV - 1) % NBV], pb);
             SVA_EXP_CHECKED(sc, pb);
-            SVA_PV(sV[u % NBV], pb);
             SVA_MASK_ONLY(lim, sn);
             sc = sn;
             __builtin_amdgcn_s_waitcnt(kWaitNext);
             __builtin_amdgcn_s_barrier();
         }
     }
+    // the last stage's product (its V landed before the loop's last barrier)
+    if (nstage > 0) SVA_PV(sV[(nstage - 1) % NBV], pb);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // no copy left in flight at exit
 
     // Compensation (sparse rows that drop blocks): every block the row does
