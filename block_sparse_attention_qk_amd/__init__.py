@@ -45,7 +45,7 @@ EXPORTED = (
     "sva_plan_create", "sva_plan_create_ex", "sva_plan_get_info", "sva_destroy",
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
     "sva_block_means", "sva_attention_compensated", "sva_qk_norm_rope_tiled",
-    "sva_attention_ex", "sva_stream_copy",
+    "sva_attention_ex", "sva_select_blocks_noalloc", "sva_stream_copy",
     "sva_status_string", "sva_last_error",
 )
 
@@ -106,6 +106,7 @@ def lib() -> ctypes.CDLL:
     L.sva_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     L.sva_reorder.argtypes = [vp, vp, vp, i, vp]
     L.sva_select_blocks.argtypes = [vp, vp, vp, vp, sz, vp, vp]
+    L.sva_select_blocks_noalloc.argtypes = [vp, vp, vp, vp, vp]
     L.sva_stream_copy.argtypes = [vp, vp, sz, vp]
     L.sva_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.sva_block_means.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -363,6 +364,18 @@ def sva_select_blocks(plan: Plan, q_r, k_t, workspace, col, stream=None) -> None
         plan.handle, _tensor(q_r, ts, torch.bfloat16, "q_r") if q_r is not None else None,
         _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t") if k_t is not None else None,
         ws, ws_bytes, _tensor(col, (int(plan.info.nnz),), torch.int32, "col"), _stream(stream)))
+
+
+def sva_select_blocks_noalloc(plan: Plan, q_r, k_t, col, stream=None) -> None:
+    """sva_select_blocks with the library's fixed device scratch in place of
+    a workspace (no allocation; calls that overlap on one GPU race)."""
+    import torch
+    if plan.info.dense:
+        return
+    _check(lib().sva_select_blocks_noalloc(
+        plan.handle, _tensor(q_r, plan.tile_shape, torch.bfloat16, "q_r"),
+        _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
+        _tensor(col, (int(plan.info.nnz),), torch.int32, "col"), _stream(stream)))
 
 
 def sva_stream_copy(dst, src, stream=None) -> None:

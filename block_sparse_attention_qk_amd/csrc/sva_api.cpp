@@ -8,8 +8,7 @@
 #include <new>
 #include <string>
 
-#include "kernels.h"
-#include "plan_host.h"
+#include "plan_dev.h"
 
 namespace sva {
 
@@ -31,13 +30,6 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 void set_last_error(const std::string& msg) { g_last_error = msg; }
 
 }  // namespace sva
-
-struct sva_plan_s {
-    sva::HostPlan host;
-    sva::DevPlan dev{};
-    int device = 0;
-    void* dmem = nullptr;   // one allocation holding every device table
-};
 
 using sva::set_err;
 
@@ -106,6 +98,12 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     if (e != hipSuccess) {
         delete plan;
         return sva::hip_err(e, "hipGetDevice");
+    }
+    // set-up of this device for sva_select_blocks_noalloc
+    e = sva::resolve_select_scratch(plan->device);
+    if (e != hipSuccess) {
+        delete plan;
+        return sva::hip_err(e, "hipGetSymbolAddress(select scratch)");
     }
     // one device buffer: perm, inv, valid, tmin, tmax, row_ptr, rope table
     auto align = [](size_t x) { return (x + 255) / 256 * 256; };

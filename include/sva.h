@@ -233,6 +233,23 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t,
                       void* workspace, size_t workspace_bytes, int32_t* col,
                       void* stream);
 
+/* Block selection that allocates nothing, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The same selection as
+ * sva_select_blocks with q_r and k_t given (pooling, then ranking), with
+ * the block means kept in a fixed device array of the library instead of
+ * a caller workspace: 128 MiB per GPU, held from the first plan created on
+ * that GPU until the process ends.  A plan whose
+ * info.select_workspace_bytes exceeds 128 MiB gets SVA_ERR_WORKSPACE before
+ * anything is enqueued (the mean scorer fits up to 48 heads × 1024 blocks
+ * at d = 128).  q_r, k_t and col as for sva_select_blocks (both inputs
+ * required); the current device must be the plan's.  Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other threads) race and may return wrong lists; order them on one
+ * stream.  Nothing to do for a dense plan. */
+int sva_select_blocks_noalloc(sva_plan plan, const void* q_r, const void* k_t, int32_t* col,
+                              void* stream);
+
 /* Attention over the kept blocks.  For each valid query row p of block qb:
  * o_p = sum_j softmax_j(q_p·k_j / sqrt(d)) v_j over the valid keys j of the
  * blocks in row qb of `col` (any ascending list with the plan's row_ptr is
