@@ -56,6 +56,8 @@ def parse():
                          "attention, inverse reorder) instead of the fused step")
     ap.add_argument("--cpu-heads", type=int, default=2,
                     help="heads the CPU oracle runs the whole step on (bounded sample)")
+    ap.add_argument("--no-copy-ref", action="store_true",
+                    help="skip the streaming-copy reference measurement")
     ap.add_argument("--no-h3-prologue", action="store_true",
                     help="skip the prologue timing at the packed video + audio model's "
                          "per-rank shape (4,722 rows, 56 heads, RoPE over 96 of 128 channels)")
@@ -248,9 +250,10 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
 
-    copy = hbm_copy(S, np, torch)
-    out["hbm_copy"] = copy
-    out["stages_vs_copy"] = {n: round(t / copy["gbs"], 4) for n, t in stage_gbs.items()}
+    if not args.no_copy_ref:
+        copy = hbm_copy(S, np, torch)
+        out["hbm_copy"] = copy
+        out["stages_vs_copy"] = {n: round(t / copy["gbs"], 4) for n, t in stage_gbs.items()}
     if not args.no_h3_prologue:
         out["h3_prologue"] = h3_prologue(S, I, np, torch, to_dev)
     if not args.no_cpu_baseline:
