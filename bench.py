@@ -135,15 +135,15 @@ def main():
             S.sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t)
         rec()
         if args.staged:
-            S.sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
-                               buf.o_r, S.SVA_LAYOUT_TILE)
+            S.sva_attention_ws(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
+                               buf.o_r, S.SVA_LAYOUT_TILE, buf.aws)
             rec()
             S.sva_reorder(plan, buf.o_r, buf.o, S.SVA_INVERSE)
             rec()
         else:
             # O straight into raster order
-            S.sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
-                               buf.o, S.SVA_LAYOUT_RASTER)
+            S.sva_attention_ws(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t,
+                               buf.o, S.SVA_LAYOUT_RASTER, buf.aws)
             rec()
 
     for _ in range(args.warmup):

@@ -45,7 +45,7 @@ EXPORTED = (
     "sva_plan_create", "sva_plan_create_ex", "sva_plan_get_info", "sva_destroy",
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
     "sva_block_means", "sva_attention_compensated", "sva_qk_norm_rope_tiled",
-    "sva_attention_ex", "sva_select_blocks_noalloc", "sva_stream_copy",
+    "sva_attention_ex", "sva_attention_ws", "sva_select_blocks_noalloc", "sva_stream_copy",
     "sva_status_string", "sva_last_error",
 )
 
@@ -79,6 +79,7 @@ class sva_plan_info(ctypes.Structure):
         ("rope_split", ctypes.c_int32 * 3),
         ("scorer", ctypes.c_int32), ("subblocks", ctypes.c_int32),
         ("budget_multiple", ctypes.c_int32), ("n_mean_groups", ctypes.c_int32),
+        ("attention_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
     L.sva_attention_compensated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.sva_qk_norm_rope_tiled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.sva_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
+    L.sva_attention_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
     L.sva_last_error.argtypes = []
@@ -430,8 +432,7 @@ def sva_attention_compensated(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o_r,
         _tensor(vm_t, plan.vm_shape, bf, "vm_t"), _tensor(o_r, ts, bf, "o_r"), _stream(stream)))
 
 
-def sva_attention_ex(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout,
-                     stream=None) -> None:
+def _attention_args(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout):
     import torch
     bf = torch.bfloat16
     c = None
@@ -442,12 +443,27 @@ def sva_attention_ex(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout,
     if (km_t is None) != (vm_t is None):
         raise ValueError("km_t and vm_t go together")
     oshape = plan.raster_shape if o_layout == SVA_LAYOUT_RASTER else plan.tile_shape
-    _check(lib().sva_attention_ex(
-        plan.handle, _tensor(q_r, plan.tile_shape, bf, "q_r"),
-        _tensor(k_t, plan.kt_shape, bf, "k_t"), _tensor(v_t, plan.vt_shape, bf, "v_t"), c,
-        _tensor(km_t, plan.km_shape, bf, "km_t") if km_t is not None else None,
-        _tensor(vm_t, plan.vm_shape, bf, "vm_t") if vm_t is not None else None,
-        _tensor(o, oshape, bf, "o"), int(o_layout), _stream(stream)))
+    return (plan.handle, _tensor(q_r, plan.tile_shape, bf, "q_r"),
+            _tensor(k_t, plan.kt_shape, bf, "k_t"), _tensor(v_t, plan.vt_shape, bf, "v_t"), c,
+            _tensor(km_t, plan.km_shape, bf, "km_t") if km_t is not None else None,
+            _tensor(vm_t, plan.vm_shape, bf, "vm_t") if vm_t is not None else None,
+            _tensor(o, oshape, bf, "o"), int(o_layout))
+
+
+def sva_attention_ex(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout,
+                     stream=None) -> None:
+    _check(lib().sva_attention_ex(*_attention_args(plan, q_r, k_t, v_t, col, km_t, vm_t, o,
+                                                   o_layout), _stream(stream)))
+
+
+def sva_attention_ws(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout, workspace,
+                     stream=None) -> None:
+    """sva_attention_ex with the plan's long rows split over several
+    workgroups; ``workspace`` (info.attention_workspace_bytes) holds their
+    partials.  workspace None: exactly sva_attention_ex."""
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().sva_attention_ws(*_attention_args(plan, q_r, k_t, v_t, col, km_t, vm_t, o,
+                                                   o_layout), ws, ws_bytes, _stream(stream)))
 
 
 def sva_status_string(status: int) -> str:
@@ -484,6 +500,8 @@ class Buffers:
             self.km_t = self.vm_t = None
         ws = int(plan.info.select_workspace_bytes)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        aws = int(plan.info.attention_workspace_bytes)
+        self.aws = torch.empty(aws, dtype=torch.uint8, device=device) if aws else None
 
 
 def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
@@ -499,8 +517,8 @@ def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
         sva_select_blocks(plan, None, None, buf.ws, buf.col, stream)
     if plan.compensated:
         sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
-    sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o,
-                     SVA_LAYOUT_RASTER, stream)
+    sva_attention_ws(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o,
+                     SVA_LAYOUT_RASTER, buf.aws, stream)
     return buf.o
 
 
@@ -515,7 +533,7 @@ def forward_staged(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
         sva_select_blocks(plan, buf.q_r, buf.k_t, buf.ws, buf.col, stream)
     if plan.compensated:
         sva_block_means(plan, buf.k_t, buf.v_t, buf.km_t, buf.vm_t, stream)
-    sva_attention_ex(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o_r,
-                     SVA_LAYOUT_TILE, stream)
+    sva_attention_ws(plan, buf.q_r, buf.k_t, buf.v_t, buf.col, buf.km_t, buf.vm_t, buf.o_r,
+                     SVA_LAYOUT_TILE, buf.aws, stream)
     sva_reorder(plan, buf.o_r, buf.o, SVA_INVERSE, stream)
     return buf.o

@@ -11,7 +11,10 @@
 // Work split: one workgroup per (b, h, qb), one wave per 32 query rows
 // (BLK/32 waves), two workgroups per CU.  A dense plan, whose rows all walk
 // every block, gives a workgroup two query blocks, so one copy of each K/V
-// stage feeds twice the waves.  A row's key blocks are consumed
+// stage feeds twice the waves.  With a partials workspace, a sparse plan's
+// rows that are much longer than the others (extra-token rows keep every
+// block) are cut into pieces, one workgroup each, each writing its
+// unnormalised O, running max and sum; a merge kernel combines them.  A row's key blocks are consumed
 // in stages of 32 keys.  Both operand streams come in MFMA-ready tile
 // layouts written by the reorder kernels (K tiles, V tiles), in which one
 // stage of K and one stage of V are each a contiguous span of 32·d bf16.
@@ -70,6 +73,7 @@ struct AttnArgs {
     const u32x4_t* vm;   // block-mean V tiles [B,H,n_mean_groups,4,d,8]
     uint2* o;            // [B,H,Np,d], or [B,N,H,d] with o_raster
     int o_raster;
+    float* part;         // partials of split rows, or NULL (no row is split)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -212,19 +216,35 @@ void attn_kernel(AttnArgs a) {
                                          // then a bitmap of it
 
     const DevPlan& p = a.p;
-    const int ngrp = (p.nB + QPW - 1) / QPW;
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int qg = (int)(wg % ngrp);     // group of QPW query blocks
-    const int64_t bh = wg / ngrp;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, hf = lane >> 5;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform copy
-    // First query block of the group.  Sparse plans start each head with
-    // the blocks of extra tokens: their rows keep every block and are the
-    // longest, so they must not be the last to begin.
-    const int nx = p.nB - p.nB_video;
-    const int qfirst = QPW == 1 ? (qg < nx ? p.nB_video + qg : qg - nx) : qg * QPW;
+    int64_t bh;
+    int qfirst;
+    // a work item of a split launch: list entries [e0, e1) of the row,
+    // partials into slot `slot` (-1: the whole row, output as usual)
+    int e0 = 0, e1 = -1, slot = -1;
+    if (QPW == 1 && a.part != nullptr) {
+        const int item = (int)(wg % p.n_items);
+        bh = wg / p.n_items;
+        const __attribute__((address_space(4))) int32_t* it =
+            (const __attribute__((address_space(4))) int32_t*)(p.items + 4 * item);
+        qfirst = it[0];
+        e0 = it[1];
+        e1 = it[2];
+        slot = it[3];
+    } else {
+        // First query block of the group.  Sparse plans start each head with
+        // the blocks of extra tokens: their rows keep every block and are the
+        // longest, so they must not be the last to begin.
+        const int ngrp = (p.nB + QPW - 1) / QPW;
+        const int qg = (int)(wg % ngrp);     // group of QPW query blocks
+        bh = wg / ngrp;
+        const int nx = p.nB - p.nB_video;
+        qfirst = QPW == 1 ? (qg < nx ? p.nB_video + qg : qg - nx) : qg * QPW;
+    }
     // this wave's query block; past the last block (odd nB, QPW = 2) the
     // wave computes on the last block's rows and stores nothing
     // (wave-uniform; readfirstlane tells the compiler, so the row's pointers
@@ -254,8 +274,9 @@ void attn_kernel(AttnArgs a) {
     float m = -1e30f, l = 0.f;
     const float c = 1.4426950408889634f / sqrtf((float)D);   // log2(e)/sqrt(d)
 
-    const int64_t r0 = p.row_ptr[qb];
-    const int len = DENSE ? p.nB : (int)(p.row_ptr[qb + 1] - r0);
+    const int full_len = DENSE ? p.nB : (int)(p.row_ptr[qb + 1] - p.row_ptr[qb]);
+    const int64_t r0 = p.row_ptr[qb] + e0;
+    const int len = e1 >= 0 ? e1 - e0 : full_len;
     const int32_t* cl = DENSE ? nullptr : a.col + bh * p.nnz_per_head + r0;
     // the same list through the constant address space: wave-uniform
     // lookups become scalar loads, which do not count against vmcnt (a
@@ -541,7 +562,7 @@ void attn_kernel(AttnArgs a) {
     // kept stages, two buffer pairs alternating.
     if constexpr (COMP) {
         const int ng = p.n_mean_groups;
-        if (len < p.nB) {
+        if (slot < 0 && full_len < p.nB) {
             uint32_t* s_kept = reinterpret_cast<uint32_t*>(s_col + p.max_row_len);
             for (int i = tid; i < ng; i += NT) s_kept[i] = 0u;
             // every wave's copies have landed and every read of the stage
@@ -617,6 +638,23 @@ void attn_kernel(AttnArgs a) {
     // (the inverse reorder fused away); padding rows have none.
     if (!q_ok) return;
     const float lt = lane_swap_sum(l);
+    if (slot >= 0) {
+        // a piece of a split row: the unnormalised O^T, m and l of row qrow
+        // into the piece's partial slot (O rows of d floats, then m, then l)
+        float* pp = a.part + (bh * p.n_slots + slot) * (int64_t)(BLK * (D + 2));
+        float4* po = reinterpret_cast<float4*>(pp + (int64_t)qrow * D);
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                po[(t * 32 + 8 * g + 4 * hf) / 4] =
+                    make_float4(o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]);
+        if (hf == 0) {
+            pp[BLK * D + qrow] = m;
+            pp[BLK * D + BLK + qrow] = lt;
+        }
+        return;
+    }
     const bool row_ok = qrow < p.blk_valid[qb];
     const float inv = (row_ok && lt > 0.f) ? 1.f / lt : 0.f;
     uint2* op;
@@ -642,11 +680,62 @@ void attn_kernel(AttnArgs a) {
         }
 }
 
+// Merge of a split row's pieces: per query row, M = max of the pieces'
+// running maxima, o = sum 2^(m_i - M) O_i / sum 2^(m_i - M) l_i (m in log2
+// units), written like the unsplit rows (tile order with zero padding rows,
+// or raster order).  One workgroup per (b, h, split row).
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void attn_merge_kernel(DevPlan p, const float* part, uint2* o,
+                                                         int o_raster) {
+    constexpr int C4 = D / 4;                   // float4 chunks per row
+    const int sr = (int)(blockIdx.x % (unsigned)p.n_split);
+    const int64_t bh = blockIdx.x / (unsigned)p.n_split;
+    const int qb = p.split_rows[3 * sr];
+    const int s0 = p.split_rows[3 * sr + 1];
+    const int np = p.split_rows[3 * sr + 2];
+    const int64_t ss = (int64_t)BLK * (D + 2);  // floats per slot
+    const float* base = part + (bh * p.n_slots + s0) * ss;
+    const int valid = p.blk_valid[qb];
+    const int64_t b = bh / p.H, h = bh - b * p.H;
+    for (int idx = threadIdx.x; idx < BLK * C4; idx += 256) {
+        const int row = idx / C4, c4 = idx - row * C4;
+        float M = -INFINITY;
+        for (int q = 0; q < np; ++q) M = fmaxf(M, base[q * ss + BLK * D + row]);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        float L = 0.f;
+        for (int q = 0; q < np; ++q) {
+            const float* sp = base + q * ss;
+            const float w = __builtin_amdgcn_exp2f(sp[BLK * D + row] - M);
+            L += w * sp[BLK * D + BLK + row];
+            const float4 v = reinterpret_cast<const float4*>(sp + (int64_t)row * D)[c4];
+            acc.x += w * v.x;
+            acc.y += w * v.y;
+            acc.z += w * v.z;
+            acc.w += w * v.w;
+        }
+        const bool row_ok = row < valid;
+        const float inv = (row_ok && L > 0.f) ? 1.f / L : 0.f;
+        uint2 wv = {0u, 0u};
+        if (row_ok) {
+            wv.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+            wv.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+        }
+        if (o_raster) {
+            if (!row_ok) continue;
+            const int n = p.inv[qb * BLK + row];
+            o[((b * p.N + n) * p.H + h) * C4 + c4] = wv;
+        } else {
+            o[((bh * p.Np) + (int64_t)qb * BLK + row) * C4 + c4] = wv;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
                             const uint16_t* vt, const int32_t* col, const uint16_t* km,
-                            const uint16_t* vm, uint16_t* o, bool o_raster, hipStream_t s) {
+                            const uint16_t* vm, uint16_t* o, bool o_raster, float* part,
+                            hipStream_t s) {
     AttnArgs a;
     a.p = p;
     a.q = reinterpret_cast<const u32x4_t*>(qr);
@@ -657,11 +746,15 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
     a.vm = reinterpret_cast<const u32x4_t*>(vm);
     a.o = reinterpret_cast<uint2*>(o);
     a.o_raster = o_raster ? 1 : 0;
+    // long rows split only for sparse plans that have split rows
+    const bool split = part != nullptr && !p.dense && p.n_items > 0;
+    a.part = split ? part : nullptr;
     // dense plans: two query blocks per workgroup, except d = 64 with
     // 128-token blocks, whose stage copy (256 chunks) cannot be split over
     // eight waves
     const int qpw = (p.dense && !(p.d == 64 && p.block == 128)) ? 2 : 1;
-    dim3 grid((unsigned)((int64_t)p.B * p.H * ((p.nB + qpw - 1) / qpw)));
+    const int64_t per_head = split ? p.n_items : (p.nB + qpw - 1) / qpw;
+    dim3 grid((unsigned)((int64_t)p.B * p.H * per_head));
     dim3 block(p.block * 2 * qpw);
     // dynamic LDS: compensation's copy of the block list and its bitmap
     const size_t lds = km ? (size_t)(p.max_row_len + p.n_mean_groups) * sizeof(int32_t) : 0;
@@ -683,6 +776,20 @@ hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t
         else if (p.d == 128) launch(attn_kernel<128, 64, false, true, 1>);
         else if (p.block == 128) launch(attn_kernel<64, 128, false, true, 1>);
         else launch(attn_kernel<64, 64, false, true, 1>);
+    }
+    if (split) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 mg((unsigned)((int64_t)p.B * p.H * p.n_split));
+        uint2* o2 = reinterpret_cast<uint2*>(o);
+        if (p.d == 128 && p.block == 128)
+            hipLaunchKernelGGL((attn_merge_kernel<128, 128>), mg, dim3(256), 0, s, p, part, o2, a.o_raster);
+        else if (p.d == 128)
+            hipLaunchKernelGGL((attn_merge_kernel<128, 64>), mg, dim3(256), 0, s, p, part, o2, a.o_raster);
+        else if (p.block == 128)
+            hipLaunchKernelGGL((attn_merge_kernel<64, 128>), mg, dim3(256), 0, s, p, part, o2, a.o_raster);
+        else
+            hipLaunchKernelGGL((attn_merge_kernel<64, 64>), mg, dim3(256), 0, s, p, part, o2, a.o_raster);
     }
     return hipGetLastError();
 }

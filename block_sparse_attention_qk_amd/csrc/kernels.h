@@ -50,6 +50,13 @@ struct DevPlan {
     const int32_t* row_ptr;    // [nB+1]
     int64_t nnz_per_head;
     int max_row_len;
+    // split long rows (attention with a workspace): n_items work items of
+    // 4 ints (qb, first entry, end entry, partial slot or -1) per (b, h),
+    // n_split split rows of 3 ints (qb, first slot, pieces), n_slots
+    // partial slots per (b, h); n_items == 0 when no row is split
+    const int32_t* items;
+    const int32_t* split_rows;
+    int n_items, n_split, n_slots;
     // divisions of (token, head) row indices, all below 2^31
     FastDiv div_H, div_N, div_HW, div_W, div_Np;
 };
@@ -71,10 +78,12 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
                          int32_t* col, hipStream_t s);
 
 // km, vm: mean tiles (NULL: no compensation); o_raster: O in raster order
-// [B,N,H,d] instead of tile order [B,H,Np,d]
+// [B,N,H,d] instead of tile order [B,H,Np,d]; part (NULL: no split): the
+// partials of split rows, then their merge into o
 hipError_t launch_attention(const DevPlan& p, const uint16_t* qr, const uint16_t* kr,
                             const uint16_t* vt, const int32_t* col, const uint16_t* km,
-                            const uint16_t* vm, uint16_t* o, bool o_raster, hipStream_t s);
+                            const uint16_t* vm, uint16_t* o, bool o_raster, float* part,
+                            hipStream_t s);
 
 hipError_t launch_block_means(const DevPlan& p, const uint16_t* kt, const uint16_t* vt,
                               uint16_t* km, uint16_t* vm, hipStream_t s);

@@ -184,6 +184,47 @@ int build_host_plan(const sva_plan_desc& in, HostPlan& p, std::string& err, bool
     I.select_workspace_bytes =
         I.dense ? 0 : (size_t)2 * d.B * d.H * nB * d.subblocks * d.d * sizeof(double);
 
+    // --- split of long rows ---
+    // A sparse plan's extra-token rows keep every block and can be many
+    // times longer than the video rows; walked by one workgroup each, they
+    // bound the step of a grid with few heads.  With an attention workspace
+    // every row longer than 1.5 times the longest video row is cut into
+    // pieces of at most that many list entries; each piece is a workgroup
+    // of its own writing (m, l, O) partials, merged afterwards.
+    p.items.clear();
+    p.split_rows.clear();
+    p.n_slots = 0;
+    if (!I.dense) {
+        int32_t chunk = 16;
+        for (int qb = 0; qb < I.nB_video; ++qb)
+            chunk = std::max(chunk, p.row_ptr[qb + 1] - p.row_ptr[qb]);
+        std::vector<char> split(nB, 0);
+        for (int qb = 0; qb < nB; ++qb) {
+            const int32_t len = p.row_ptr[qb + 1] - p.row_ptr[qb];
+            if (2 * len <= 3 * chunk) continue;
+            const int32_t pieces = (len + chunk - 1) / chunk;
+            split[qb] = 1;
+            p.split_rows.insert(p.split_rows.end(), {qb, p.n_slots, pieces});
+            for (int32_t q = 0; q < pieces; ++q) {
+                const int32_t e0 = (int32_t)((int64_t)len * q / pieces);
+                const int32_t e1 = (int32_t)((int64_t)len * (q + 1) / pieces);
+                p.items.insert(p.items.end(), {qb, e0, e1, p.n_slots + q});
+            }
+            p.n_slots += pieces;
+        }
+        if (p.n_slots > 0) {
+            for (int qb = 0; qb < nB; ++qb)
+                if (!split[qb])
+                    p.items.insert(p.items.end(),
+                                   {qb, 0, p.row_ptr[qb + 1] - p.row_ptr[qb], -1});
+        } else {
+            p.items.clear();
+        }
+    }
+    // partials: per slot, O (block x d), then m and l (block each), float32
+    I.attention_workspace_bytes =
+        (size_t)d.B * d.H * p.n_slots * d.block * (d.d + 2) * sizeof(float);
+
     // --- RoPE tables ---
     if (with_tables) {
         const int len[3] = {d.T, d.Hh, d.W};

@@ -20,6 +20,13 @@ struct HostPlan {
     std::vector<int32_t> blk_tmin;   // [nB] first frame of the valid tokens (-1 extra)
     std::vector<int32_t> blk_tmax;   // [nB] last frame (-1 extra)
     std::vector<int32_t> row_ptr;    // [nB+1]
+    // Attention work items when long rows are split (sva_attention_ws):
+    // 4 ints per item (qb, first list entry, end entry, partial slot or -1),
+    // the pieces of the split rows first; split rows: 3 ints per row (qb,
+    // first slot, pieces).
+    std::vector<int32_t> items;
+    std::vector<int32_t> split_rows;
+    int32_t n_slots = 0;     // partial slots per (b, h)
     // RoPE cos/sin per axis section: entry (pos, i) of axis a at
     // rope_off[a] + pos * rope_half[a] + i, as (cos, sin) pairs.
     std::vector<float> rope_cs;

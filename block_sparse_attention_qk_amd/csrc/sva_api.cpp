@@ -110,7 +110,8 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     const size_t s_perm = align(h.perm.size() * 4), s_inv = align(h.inv.size() * 4);
     const size_t s_blk = align(h.blk_valid.size() * 4), s_rp = align(h.row_ptr.size() * 4);
     const size_t s_rope = align(h.rope_cs.size() * 4);
-    const size_t total = s_perm + s_inv + 3 * s_blk + s_rp + s_rope;
+    const size_t s_items = align(h.items.size() * 4), s_split = align(h.split_rows.size() * 4);
+    const size_t total = s_perm + s_inv + 3 * s_blk + s_rp + s_rope + s_items + s_split;
     e = hipMalloc(&plan->dmem, total);
     if (e != hipSuccess) {
         delete plan;
@@ -132,6 +133,11 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.blk_tmax = static_cast<const int32_t*>(put(h.blk_tmax.data(), h.blk_tmax.size() * 4, s_blk));
     d.row_ptr = static_cast<const int32_t*>(put(h.row_ptr.data(), h.row_ptr.size() * 4, s_rp));
     d.rope_cs = static_cast<const float2*>(put(h.rope_cs.data(), h.rope_cs.size() * 4, s_rope));
+    d.items = static_cast<const int32_t*>(put(h.items.data(), h.items.size() * 4, s_items));
+    d.split_rows = static_cast<const int32_t*>(put(h.split_rows.data(), h.split_rows.size() * 4, s_split));
+    d.n_items = (int)(h.items.size() / 4);
+    d.n_split = (int)(h.split_rows.size() / 3);
+    d.n_slots = h.n_slots;
     if (e != hipSuccess) {
         (void)hipFree(plan->dmem);   // the copy error is the one reported
         delete plan;
@@ -268,9 +274,9 @@ int sva_select_blocks(sva_plan plan, const void* q_r, const void* k_t, void* wor
     return SVA_OK;
 }
 
-int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+int sva_attention_ws(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                      const int32_t* col, const void* km_t, const void* vm_t, void* o,
-                     int o_layout, void* stream) {
+                     int o_layout, void* workspace, size_t workspace_bytes, void* stream) {
     if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
     if (!q_r || !k_t || !v_t || !o)
         return set_err(SVA_ERR_INVALID_ARG, "q_r, k_t, v_t and the output must be non-NULL");
@@ -282,18 +288,31 @@ int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void
         return set_err(SVA_ERR_INVALID_ARG, "col must be non-NULL for a sparse plan");
     if (!sva::aligned16(q_r) || !sva::aligned16(k_t) || !sva::aligned16(v_t) ||
         !sva::aligned16(o) || !sva::aligned16(km_t) || !sva::aligned16(vm_t) ||
-        ((uintptr_t)col & 3u))
+        ((uintptr_t)col & 3u) || !sva::aligned16(workspace))
         return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    float* part = nullptr;
+    if (workspace && plan->host.info.attention_workspace_bytes > 0) {
+        if (workspace_bytes < plan->host.info.attention_workspace_bytes)
+            return set_err(SVA_ERR_WORKSPACE, "workspace smaller than attention_workspace_bytes");
+        part = static_cast<float*>(workspace);
+    }
     hipError_t e = sva::launch_attention(plan->dev, static_cast<const uint16_t*>(q_r),
                                          static_cast<const uint16_t*>(k_t),
                                          static_cast<const uint16_t*>(v_t), col,
                                          static_cast<const uint16_t*>(km_t),
                                          static_cast<const uint16_t*>(vm_t),
                                          static_cast<uint16_t*>(o),
-                                         o_layout == SVA_LAYOUT_RASTER,
+                                         o_layout == SVA_LAYOUT_RASTER, part,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return sva::hip_err(e, "attention launch");
     return SVA_OK;
+}
+
+int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+                     const int32_t* col, const void* km_t, const void* vm_t, void* o,
+                     int o_layout, void* stream) {
+    return sva_attention_ws(plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout, nullptr, 0,
+                            stream);
 }
 
 int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,

@@ -153,6 +153,8 @@ typedef struct {
     int32_t budget_multiple; /* resolved budget multiple                    */
     int32_t n_mean_groups;/* ceil(nB / 32): groups of 32 block means in the
                              mean tiles of sva_block_means                  */
+    size_t attention_workspace_bytes; /* workspace sva_attention_ws uses to
+                             split long rows (0: no row is split)           */
 } sva_plan_info;
 
 /* ---- host-only calls (no device needed) ---- */
@@ -260,6 +262,27 @@ int sva_select_blocks_noalloc(sva_plan plan, const void* q_r, const void* k_t, i
  * o_r: [B, H, Np, d], padding rows written as zero. */
 int sva_attention(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                   const int32_t* col, void* o_r, void* stream);
+
+/* sva_attention_ex with long rows split over several workgroups.  Rows
+ * that keep every key block (the extra-token rows of a sparse plan) can be
+ * many times longer than the video rows; walked by one workgroup each they
+ * bound the step when there are few heads.  With a workspace of at least
+ * info.attention_workspace_bytes (device memory, 16-byte aligned) every
+ * row longer than 1.5 times the longest video row is cut into pieces of
+ * at most that many list entries: each piece keeps its own running max m,
+ * sum l and unnormalised output O (float32, in the workspace), and a merge
+ * writes o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, M = max_i m_i
+ * (the online-softmax merge of partial results; the rows it serves are
+ * those of the audio tokens that the "内核层" section of the MiniMax-H3
+ * page packs into one sequence with the video tokens).  The result equals
+ * sva_attention_ex up to float rounding
+ * order.  workspace NULL, or a plan with attention_workspace_bytes == 0:
+ * exactly sva_attention_ex.  Other arguments as for sva_attention_ex;
+ * compensated plans compensate the unsplit rows only (a split row keeps
+ * every block). */
+int sva_attention_ws(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
+                     const int32_t* col, const void* km_t, const void* vm_t, void* o,
+                     int o_layout, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Block means for compensation.  From the K tiles and V tiles of a step,
  * the mean key and mean value of every key block over its valid tokens

@@ -399,6 +399,64 @@ def test_attention_out_of_range_entries():
         assert max_abs(out[0, h][rows], ref[rows]) <= MAX_ABS
 
 
+# rows that keep every block (extra tokens) split over several workgroups:
+# 64-token blocks, 60 video + 2 extra blocks, 7 kept per video row, so each
+# extra row is cut into 4 pieces; 128-token blocks with B = 2, same-frame
+# forcing and 2 extra blocks (47 blocks, 3 pieces per extra row); and a
+# compensated plan (its split rows keep every block, the video rows still
+# compensate what they drop)
+SPLIT = {
+    "split64": I.custom("split64", 1, 2, 4, 16, 60, 64, 64, 0.9, tile=(4, 4, 4), n_extra=128,
+                        seed_base=12100),
+    "split128": I.custom("split128", 2, 2, 6, 24, 40, 128, 128, 0.85, tile=(2, 8, 8),
+                         n_extra=256, flags=I.KEEP_SAME_FRAME, temperature=True,
+                         seed_base=12200),
+    "split_comp": I.custom("split_comp", 1, 2, 4, 16, 60, 128, 64, 0.9, tile=(4, 4, 4),
+                           n_extra=128, flags=I.COMPENSATE, seed_base=12300),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT))
+def test_split_rows(name):
+    """sva_attention_ws splits the extra-token rows into pieces merged by
+    (m, l, O): the output matches the oracle (whole step, every head), the
+    unsplit call matches it too, and the split raster output equals the
+    split tile-order output after the inverse reorder, bit for bit."""
+    wl = SPLIT[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    g = geometry(wl)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    info = run.plan.info
+    assert info.attention_workspace_bytes > 0 and run.buf.aws is not None
+    run.run()                                   # staged: tile-order split output
+    b = run.buf
+    o_ras = torch.empty(run.plan.raster_shape, dtype=torch.bfloat16, device="cuda")
+    S.sva_attention_ws(run.plan, b.q_r, b.k_t, b.v_t, b.col, b.km_t, b.vm_t, o_ras,
+                       S.SVA_LAYOUT_RASTER, b.aws)
+    o_un = torch.empty(run.plan.tile_shape, dtype=torch.bfloat16, device="cuda")
+    S.sva_attention_ex(run.plan, b.q_r, b.k_t, b.v_t, b.col, b.km_t, b.vm_t, o_un,
+                       S.SVA_LAYOUT_TILE)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o_ras), host(b.o))
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    out = host_f64(b.o)
+    un = host_f64(o_un)
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for bb in range(wl.B):
+        for h in range(wl.H):
+            r = O.run_head(O.bf16_bits_to_f64(q[bb, :, h]), O.bf16_bits_to_f64(k[bb, :, h]),
+                           O.bf16_bits_to_f64(v[bb, :, h]), wq[h], wk[h], g, perm=perm, meta=meta)
+            worst[0] = max(worst[0], rel_l2(out[bb, :, h], r["o"]))
+            worst[1] = max(worst[1], max_abs(out[bb, :, h], r["o"]))
+            worst[2] = max(worst[2], rel_l2(un[bb, h], r["o_r"]))
+            worst[3] = max(worst[3], max_abs(un[bb, h], r["o_r"]))
+    print(f"{name}: split rel_l2 {worst[0]:.2e} max_abs {worst[1]:.2e}; unsplit rel_l2 "
+          f"{worst[2]:.2e} max_abs {worst[3]:.2e}; workspace {info.attention_workspace_bytes} B")
+    assert worst[0] <= REL_L2 and worst[1] <= MAX_ABS
+    assert worst[2] <= REL_L2 and worst[3] <= MAX_ABS
+
+
 _GROWTH = ["ragged128", "ragged64", "d128_b64", "dense128"]
 
 
@@ -496,8 +554,8 @@ def test_raster_output_is_inverse_reorder(name):
     o_ras.fill_(_NAN_BITS)
     o_ras = o_ras.view(torch.bfloat16)
     b = run.buf
-    S.sva_attention_ex(run.plan, b.q_r, b.k_t, b.v_t, b.col, b.km_t, b.vm_t, o_ras,
-                       S.SVA_LAYOUT_RASTER)
+    S.sva_attention_ws(run.plan, b.q_r, b.k_t, b.v_t, b.col, b.km_t, b.vm_t, o_ras,
+                       S.SVA_LAYOUT_RASTER, b.aws)
     torch.cuda.synchronize()
     assert np.array_equal(host(o_ras), host(b.o))
 
