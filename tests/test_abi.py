@@ -66,6 +66,22 @@ def test_host_plan_equals_oracle(wl):
         assert np.array_equal(forced.astype(bool), want)
 
 
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_split_workspace_size(wl):
+    """The partials workspace of sva_attention_ws: in a sparse plan every
+    row longer than 1.5 times the longest video row (at least 16) is cut
+    into ceil(len / that) pieces, each slot holding block x (d + 2) floats
+    per (b, h); no row is split in a dense plan."""
+    g = _geom(wl)
+    info = S.sva_plan_query(S.desc_for(wl))
+    lens = O.row_lengths(g)
+    slots = 0
+    if not g.dense:
+        chunk = max(16, int(lens[: g.nB_video].max()))
+        slots = sum(-(-int(n) // chunk) for n in lens if 2 * n > 3 * chunk)
+    assert info.attention_workspace_bytes == wl.B * wl.H * slots * g.block * (g.d + 2) * 4
+
+
 def test_workload_block_lists():
     """The executed block pairs of the bench workload (75,600 tokens,
     128-token blocks, sparsity 0.75): 591 rows of 148 blocks per head."""
