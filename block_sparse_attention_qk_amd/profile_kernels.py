@@ -4,7 +4,8 @@
         python3 bench.py --workload W --steps 5 --warmup 1 --no-cpu-baseline \\
         --no-h3-prologue --no-copy-ref
     python -m block_sparse_attention_qk_amd.profile_kernels --stats DIR/bench_kernel_stats.csv \\
-        --bench-json B.json --title "..." --command "..." --out-md F.md
+        --trace DIR/bench_kernel_trace.csv --bench-json B.json --title "..." \\
+        --command "..." --out-md F.md
 
 The statistics file gives calls and average, minimum and maximum duration
 per kernel; ``--bench-json`` adds the bench line of the same box (the
@@ -27,6 +28,21 @@ def _short(name: str) -> str:
     return name.split("(")[0].strip()
 
 
+def read_medians(trace_path: str) -> dict:
+    """Median duration (ms) per kernel from a kernel-trace csv."""
+    per = {}
+    with open(trace_path) as fh:
+        for r in csv.DictReader(fh):
+            per.setdefault(_short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+    out = {}
+    for k, v in per.items():
+        v = sorted(v)
+        n = len(v)
+        out[k] = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return out
+
+
 def read_stats(path: str):
     rows = []
     with open(path) as fh:
@@ -43,20 +59,27 @@ def read_stats(path: str):
     return rows
 
 
-def to_markdown(rows, title, command, bench=None, flop=None):
+def to_markdown(rows, title, command, bench=None, flop=None, medians=None):
+    medians = medians or {}
     lines = [f"# {title}", "", "Command (from the repository root, on the machine with the GPU):",
              "", "```", command, "```", "",
-             "| kernel | calls | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg ms | median ms | min ms | max ms | share |",
+             "|---|---|---|---|---|---|---|"]
     for e in rows:
-        lines.append(f"| `{e['kernel']}` | {e['calls']} | {e['avg_ms']:.3f} | {e['min_ms']:.3f} | "
-                     f"{e['max_ms']:.3f} | {e['share']:.2f}% |")
+        med = medians.get(e["kernel"])
+        ms = f"{med:.3f}" if med is not None else "—"
+        lines.append(f"| `{e['kernel']}` | {e['calls']} | {e['avg_ms']:.3f} | {ms} | "
+                     f"{e['min_ms']:.3f} | {e['max_ms']:.3f} | {e['share']:.2f}% |")
     attn = [e for e in rows if e["kernel"].startswith("attn_kernel")]
     if flop and attn:
         a = attn[0]
-        tf = flop / (a["avg_ms"] * 1e-3) / 1e12
-        lines += ["", f"Attention from this profile: {flop / 1e12:.3f} TFLOP executed / "
-                      f"{a['avg_ms']:.3f} ms = {tf:.1f} TFLOP/s = {tf / PEAK_BF16_TFLOPS:.4f} of "
-                      f"{PEAK_BF16_TFLOPS} TFLOP/s (bf16 dense)."]
+        for label, t in (("average", a["avg_ms"]), ("median", medians.get(a["kernel"]))):
+            if t is None:
+                continue
+            tf = flop / (t * 1e-3) / 1e12
+            lines += ["", f"Attention from this profile ({label}): {flop / 1e12:.3f} TFLOP executed / "
+                          f"{t:.3f} ms = {tf:.1f} TFLOP/s = {tf / PEAK_BF16_TFLOPS:.4f} of "
+                          f"{PEAK_BF16_TFLOPS} TFLOP/s (bf16 dense)."]
     if bench:
         r = bench.get("roofline", {})
         lines += ["", "bench.py on the same box (median of the per-call HIP event times):", "",
@@ -70,6 +93,7 @@ def to_markdown(rows, title, command, bench=None, flop=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats", required=True)
+    ap.add_argument("--trace", help="kernel-trace csv of the same run (per-dispatch medians)")
     ap.add_argument("--bench-json")
     ap.add_argument("--flop", type=float, default=None,
                     help="executed attention flops per call (4 block^2 d nnz)")
@@ -85,8 +109,9 @@ def main():
     if flop is None and bench:
         flop = bench.get("config", {}).get("executed_attn_tflop", 0) * 1e12 or None
     rows = read_stats(a.stats)
+    medians = read_medians(a.trace) if a.trace else None
     with open(a.out_md, "w") as fh:
-        fh.write(to_markdown(rows, a.title, a.command, bench, flop))
+        fh.write(to_markdown(rows, a.title, a.command, bench, flop, medians))
     for e in rows:
         print(f"{e['kernel']:50s} {e['calls']:4d} {e['avg_ms']:9.3f} ms")
 
