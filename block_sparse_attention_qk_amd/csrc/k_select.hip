@@ -20,15 +20,20 @@
 //         order and K' as the attention kernel's K tiles, once each).  q
 //         means are stored [B,H,nB,d], k means transposed [B,H,d,nB] so the
 //         score loop reads them coalesced.
-//  topk   one workgroup per (b, h, R <= 8 query blocks): float64 scores of
-//         the R rows against every key block into LDS (each thread computes
-//         two rows against four consecutive key runs, so one LDS read of the
-//         query means feeds four fma; reading them once per fma would make
-//         the loop bound by LDS bandwidth), then one wave per row
+//  topk   one workgroup per (b, h, R <= 8 query blocks): scores of the R
+//         rows against every key block into LDS, then one wave per row
 //         finds the r-th largest eligible score by a bitwise search on
 //         order-preserving 64-bit keys (ballot + popcount, no sorting),
 //         takes equal scores lowest index first, and writes the kept
 //         block indices in ascending order with ballot prefix counts.
+//         Mean scorer: float64 fma chains, a thread per key block.  SubBlock
+//         scorer: the run products on the fp64 matrix cores; the terms
+//         exp(x - max) and the final log from the fp32 exponential and log
+//         units, the sum of the terms in float64.  Measured on gfx950, 2^y is
+//         within 8.3e-8 relative and log2 within 2.4e-7 absolute on [1, 16],
+//         so a score is within about 4e-7 of its float64 value (scores of
+//         full blocks are several units: log c_a c_b alone is 5.5 for
+//         16-token runs).
 #include "kernels.h"
 
 namespace sva {
@@ -123,6 +128,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kt_kernel(DevPlan p, const 
     }
 }
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr double kLog2e = 1.4426950408889634;
+constexpr double kLn2 = 0.6931471805599453;
+
 constexpr int kTopkThreads = 256;
 // bytes of LDS for the q means and score rows: up to 8 rows per workgroup
 // (each row costs nB·8 bytes); large enough for 4 rows at the plan's
@@ -154,6 +163,21 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
     return v;
 }
 
+// v from lane l ^ o (o = 1 or 2: within the lane's quad), by DPP quad permutation
+__device__ __forceinline__ double quad_xor(double v, int o) {
+    const int64_t u = __double_as_longlong(v);
+    const int lo = (int)u, hi = (int)(u >> 32);
+    int rlo, rhi;
+    if (o == 1) {          // quad_perm [1, 0, 3, 2]
+        rlo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+        rhi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false);
+    } else {               // quad_perm [2, 3, 0, 1]
+        rlo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+        rhi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false);
+    }
+    return __longlong_as_double(((int64_t)rhi << 32) | (uint32_t)rlo);
+}
+
 // valid tokens of run a of block b
 __device__ __forceinline__ int run_count(const DevPlan& p, int b, int a) {
     const int sb = p.block / p.nsub;
@@ -165,9 +189,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
     constexpr int RT = 8;              // rows per workgroup pass (R <= RT)
-    constexpr int DB = 4;              // channels of key means loaded per batch
-    constexpr int QW = RT * NSUB;      // query runs held in LDS
-    constexpr int QT = 2 * NSUB;       // query runs per thread (two rows)
+    constexpr int QW = SUBBLOCK ? ((RT * NSUB + 15) / 16) * 16 : RT * NSUB;   // query runs in LDS
     extern __shared__ double smem[];
     double* qs = smem;                 // [D][QW], rows past nrows zero
     double* sc = smem + QW * D;        // [R][nB]
@@ -179,9 +201,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     const int qb0 = g * R;
     const int nrows = min(R, nB - qb0);
 
-    for (int i = threadIdx.x; i < QW * D; i += kTopkThreads) {
-        const int dd = i / QW, ra = i % QW;
-        qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
+    if constexpr (!SUBBLOCK) {
+        for (int i = threadIdx.x; i < QW * D; i += kTopkThreads) {
+            const int dd = i / QW, ra = i % QW;
+            qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
+        }
+    } else {
+        // [MT][D/4][64]: entry (mt, s, l) is A[l % 16][l / 16] of step s of
+        // query tile mt, i.e. run 16mt + 4(m % 4) + m / 4 (m = l % 16), channel 4s + l / 16
+        constexpr int QN = ((RT * NSUB + 15) / 16) * (D / 4) * 64;
+        for (int i = threadIdx.x; i < QN; i += kTopkThreads) {
+            const int l = i & 63, s = (i >> 6) % (D / 4), mt = i / (64 * (D / 4));
+            const int m = l & 15;
+            const int ra = mt * 16 + 4 * (m & 3) + (m >> 2);
+            qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + 4 * s + (l >> 4)] : 0.0;
+        }
     }
     if (SUBBLOCK)
         for (int c = threadIdx.x; c <= p.block; c += kTopkThreads)
@@ -219,97 +253,111 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                 if (r < nrows) sc[r * nB + kb] = acc[r];
         }
     } else {
-        // SubBlock scorer, as a register-blocked product: thread (kg, rp) =
-        // (t / 4, t % 4) holds the QT query runs of rows 2rp, 2rp + 1 against
-        // the 4 consecutive key runs ks0 .. ks0 + 3 (run ks = kb·NSUB + b of the
-        // transposed key means).  Per channel: QT query values from LDS (one
-        // address per lane quad), 4 key values, 4·QT fma, each a sequential
-        // chain over the channels; one LDS read feeds four fma (one per fma
-        // would make the loop bound by LDS bandwidth).  NSUB divides 4, so a
-        // thread holds every key run of its key blocks and finishes the estimate
-        //   log sum_a sum_b c_a c_b exp(qbar_a · kbar_b / sqrt(d))
-        // itself.
+        // SubBlock scorer on the fp64 matrix cores: the score tile of 16
+        // query runs x 16 key runs is a sum of D/4 v_mfma_f64_16x16x4f64
+        // (A = query means, 16 runs x 4 channels; B = key means, 4 channels
+        // x 16 runs).  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+        // and receives C[l / 16 + 4i][l % 16], i = 0..3.  A rows are ordered
+        // so that a lane's four results are four consecutive query runs
+        // (A row m holds query run 4(m % 4) + m / 4), i.e. whole query
+        // blocks when NSUB divides 4; the NSUB key runs of a key block sit
+        // in NSUB neighbouring lanes.  The query operands were staged in
+        // LDS in lane order (one conflict-free 8-byte read per lane and
+        // MFMA); each wave streams 16-run key tiles from the transposed key
+        // means, the next tile loading while the current one is multiplied,
+        // and finishes
+        //   log sum_a sum_b c_a c_b exp(qbar_a . kbar_b / sqrt(d))
+        // with the NSUB x NSUB terms spread over NSUB lanes and registers.
+        constexpr int MT = (RT * NSUB + 15) / 16;
+        constexpr int KS = D / 4;
         const int nks = nB * NSUB;
-        const int rp = threadIdx.x & 3, kg = threadIdx.x >> 2;
+        const int ntile = (nks + 15) / 16;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int g4 = lane >> 4, n16 = lane & 15;
         const double inv_sqrt_d = 1.0 / sqrt((double)D);
-        double lq[2][NSUB];   // log valid counts of this thread's query runs
+        double lq[MT][4];     // log valid counts of this lane's query runs
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int aa = 0; aa < NSUB; ++aa)
-                lq[rr][aa] = lgt[run_count(p, qb0 + min(2 * rp + rr, nrows - 1), aa)];
-        for (int ks0 = kg * 4; ks0 < nks; ks0 += kTopkThreads) {
-            double acc[QT][4];
-#pragma unroll
-            for (int a2 = 0; a2 < QT; ++a2)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[a2][j] = 0.0;
-            int kcol[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kcol[j] = min(ks0 + j, nks - 1);
-            // key means in batches of DB channels, the next batch loaded
-            // while the current one is multiplied
-            double kn[DB][4];
-#pragma unroll
-            for (int i = 0; i < DB; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kn[i][j] = kt[(int64_t)i * nks + kcol[j]];
-            for (int d0 = 0; d0 < D; d0 += DB) {
-                double kv[DB][4];
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) kv[i][j] = kn[i][j];
-                if (d0 + DB < D) {
-#pragma unroll
-                    for (int i = 0; i < DB; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            kn[i][j] = kt[(int64_t)(d0 + DB + i) * nks + kcol[j]];
-                }
-#pragma unroll
-                for (int i = 0; i < DB; ++i) {
-                    const double2* q2 = reinterpret_cast<const double2*>(qs + (d0 + i) * QW + rp * QT);
-#pragma unroll
-                    for (int a2 = 0; a2 < QT / 2; ++a2) {
-                        const double2 qq = q2[a2];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            acc[2 * a2][j] = fma(qq.x, kv[i][j], acc[2 * a2][j]);
-                            acc[2 * a2 + 1][j] = fma(qq.y, kv[i][j], acc[2 * a2 + 1][j]);
-                        }
-                    }
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int j = mt * 16 + 4 * g4 + i;
+                const int row = j / NSUB;
+                lq[mt][i] = row < nrows ? lgt[run_count(p, qb0 + row, j % NSUB)] : 0.0;
             }
+        // key means of this (b, h) through a buffer resource: per-lane byte
+        // offset of (channel l / 16, run), plus a scalar offset per 4-channel step
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)kt, (short)0, D * nks * (int)sizeof(double), 0x00020000);
+        // the valid count of the lane's key block is loaded first, with the
+        // tile's key means (loads complete in order: a later global read
+        // would wait for the whole prefetch)
+        auto load_tile = [&](double (&b)[KS], int& nval, int t) {
+            const int ksc = min(t * 16 + n16, nks - 1);
+            nval = p.blk_valid[ksc / NSUB];
+            const int voff = (g4 * nks + ksc) * (int)sizeof(double);
 #pragma unroll
-            for (int kk = 0; kk < 4 / NSUB; ++kk) {
-                const int kb = ks0 / NSUB + kk;
-                double lk[NSUB];
+            for (int s = 0; s < KS; ++s)
+                b[s] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      krs, voff, 4 * s * nks * (int)sizeof(double), 0));
+        };
+        const int sb = p.block / NSUB;   // tokens per run
+        auto score_tile = [&](const double (&b)[KS], int nval, int t) {
+            f64x4_t c[MT];
 #pragma unroll
-                for (int bb = 0; bb < NSUB; ++bb) lk[bb] = lgt[run_count(p, min(kb, nB - 1), bb)];
+            for (int mt = 0; mt < MT; ++mt) c[mt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    double x[NSUB][NSUB];
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    c[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(qs[(mt * KS + s) * 64 + lane], b[s],
+                                                                 c[mt], 0, 0, 0);
+            const int ks = t * 16 + n16;
+            const int kb = ks / NSUB;
+            const double lk = lgt[min(max(nval - (ks % NSUB) * sb, 0), sb)];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int gr = 0; gr < 4 / NSUB; ++gr) {
+                    double x[NSUB];
                     double m = -INFINITY;
 #pragma unroll
-                    for (int aa = 0; aa < NSUB; ++aa)
-#pragma unroll
-                        for (int bb = 0; bb < NSUB; ++bb) {
-                            x[aa][bb] = acc[rr * NSUB + aa][kk * NSUB + bb] * inv_sqrt_d +
-                                        lq[rr][aa] + lk[bb];
-                            m = fmax(m, x[aa][bb]);
-                        }
-                    double sum = 0.0;
-                    if (m > -INFINITY) {
-#pragma unroll
-                        for (int aa = 0; aa < NSUB; ++aa)
-#pragma unroll
-                            for (int bb = 0; bb < NSUB; ++bb) sum += exp(x[aa][bb] - m);
+                    for (int a = 0; a < NSUB; ++a) {
+                        x[a] = c[mt][gr * NSUB + a] * inv_sqrt_d + lq[mt][gr * NSUB + a] + lk;
+                        m = fmax(m, x[a]);
                     }
-                    const int r = 2 * rp + rr;
-                    if (r < nrows && kb < nB) sc[r * nB + kb] = m + log(sum);
+#pragma unroll
+                    for (int o = 1; o < NSUB; o <<= 1) m = fmax(m, quad_xor(m, o));
+                    // every term -inf (no valid token pairs): sum 0, score -inf
+                    const double mm = m > -INFINITY ? m : 0.0;
+                    // terms exp(x - m) in (0, 1] from the fp32 exponential
+                    // unit (2^y, y = (x - m) log2 e), summed in fp64
+                    double sum = 0.0;
+#pragma unroll
+                    for (int a = 0; a < NSUB; ++a)
+                        sum += (double)__builtin_amdgcn_exp2f((float)((x[a] - mm) * kLog2e));
+#pragma unroll
+                    for (int o = 1; o < NSUB; o <<= 1) sum += quad_xor(sum, o);
+                    const int row = (mt * 16 + 4 * g4) / NSUB + gr;
+                    if (n16 % NSUB == 0 && row < nrows && kb < nB)
+                        sc[row * nB + kb] = m + kLn2 * (double)__builtin_amdgcn_logf((float)sum);
                 }
-            }
+        };
+        // One tile per iteration: the tile loaded during the previous one is
+        // copied out, the next one's loads are issued, then the products.
+        // The loads are issued unconditionally (tile index clamped): a load
+        // under a condition makes the compiler wait, at the first product,
+        // for the loads of the tile after it as well.
+        double bn[KS];
+        int vn;
+        load_tile(bn, vn, min(wave, ntile - 1));
+        for (int t = wave; t < ntile; t += 4) {
+            double bc[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) bc[s] = bn[s];
+            const int vc = vn;
+            load_tile(bn, vn, min(t + 4, ntile - 1));
+            __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the products
+            score_tile(bc, vc, t);
         }
     }
     __syncthreads();
@@ -425,7 +473,8 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     }
     // rows per workgroup: up to 8, as many as the score rows' LDS allows
     // next to the query runs (8 rows × nsub runs × d)
-    const int qbytes = 8 * p.nsub * p.d * (int)sizeof(double);
+    const int qruns = p.scorer == 0 ? 8 : (8 * p.nsub + 15) / 16 * 16;
+    const int qbytes = qruns * p.d * (int)sizeof(double);
     int R = (kScoreLds - qbytes) / (p.nB * (int)sizeof(double));
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
     const int groups = (p.nB + R - 1) / R;
