@@ -2,9 +2,9 @@
 
 One step = QK-RMSNorm + 3D-RoPE written straight into the attention layouts,
 reorder of V into V tiles, block selection, block-sparse attention writing O
-straight into raster order (``--staged``: the same with separate reorders
-of Q', K' and O), on synthetic inputs
-already resident in HBM.  Default workload: Wan2.1-14B-like 720p latent
+straight into raster order, in one sva_forward call whose marks time each
+stage (``--staged``: one call per stage, with separate reorders of Q', K'
+and O), on synthetic inputs already resident in HBM.  Default workload: Wan2.1-14B-like 720p latent
 grid 21×45×80 = 75,600 tokens, 40 heads, d 128, 128-token blocks,
 sparsity 0.75, same-frame key blocks always kept.
 
@@ -98,8 +98,15 @@ def main():
         names = ["prologue", "reorder_qk", "reorder_v", "select", "means", "attention", "reorder_o"]
     else:
         names = ["prologue", "reorder_v", "select", "means", "attention"]
+    n_marks = len(names) + 1
+    assert args.staged or n_marks == S.SVA_FORWARD_MARKS
 
     def step(ev=None):
+        if not args.staged:
+            # the whole step in one library call; its marks bracket the
+            # stages: prologue, V reorder, select, means, attention
+            S.forward(plan, dq, dk, dv, dwq, dwk, buf, marks=ev)
+            return
         # ev: len(names) + 1 events bracketing the stages of this step
         k = [0]
 
@@ -164,8 +171,11 @@ def main():
     rounds = min(10, args.steps)
     calls = args.steps // rounds
     nsteps = rounds * calls
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks)]
               for _ in range(nsteps)]
+    for e in events:           # torch creates an event when it is first recorded
+        for x in e:
+            x.record(stream)
     rs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(rounds)]
     torch.cuda.synchronize()
@@ -181,8 +191,10 @@ def main():
     per_call = [e[0].elapsed_time(e[-1]) for e in events]
     ms_step = float(np.median(per_call))
 
-    stage = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in events]))
-             for i, n in enumerate(names)}
+    def med(i, j):
+        return float(np.median([e[i].elapsed_time(e[j]) for e in events]))
+
+    stage = {n: med(i, i + 1) for i, n in enumerate(names)}
 
     b, d, H, B = wl.block, wl.d, wl.H, wl.B
     nnz = int(info.nnz)
@@ -231,7 +243,7 @@ def main():
             "grid": f"{wl.T}x{wl.Hh}x{wl.W}", "tokens": N, "n_extra": wl.n_extra,
             "block": b, "sparsity": wl.sparsity, "keep_same_frame": bool(wl.flags & I.KEEP_SAME_FRAME),
             "dense": bool(info.dense), "kept_block_pairs": nnz,
-            "path": "staged" if args.staged else "fused",
+            "path": "staged" if args.staged else "fused (one sva_forward call)",
             "executed_attn_tflop": round(attn_flop / 1e12, 3),
         },
         "roofline": {

@@ -46,8 +46,18 @@ EXPORTED = (
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
     "sva_block_means", "sva_attention_compensated", "sva_qk_norm_rope_tiled",
     "sva_attention_ex", "sva_attention_ws", "sva_select_blocks_noalloc", "sva_stream_copy",
-    "sva_status_string", "sva_last_error",
+    "sva_forward", "sva_status_string", "sva_last_error",
 )
+
+SVA_FORWARD_MARKS = 6
+
+
+class sva_step_buffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k", "v", "wq", "wk", "q_r", "k_t", "v_t", "select_ws")] + [
+        ("select_ws_bytes", ctypes.c_size_t), ("col", ctypes.c_void_p),
+        ("km_t", ctypes.c_void_p), ("vm_t", ctypes.c_void_p), ("attn_ws", ctypes.c_void_p),
+        ("attn_ws_bytes", ctypes.c_size_t), ("o", ctypes.c_void_p)]
 
 
 class sva_plan_desc(ctypes.Structure):
@@ -115,6 +125,7 @@ def lib() -> ctypes.CDLL:
     L.sva_qk_norm_rope_tiled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.sva_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.sva_attention_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, vp]
+    L.sva_forward.argtypes = [vp, P(sva_step_buffers), vp, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
     L.sva_last_error.argtypes = []
@@ -466,6 +477,50 @@ def sva_attention_ws(plan: Plan, q_r, k_t, v_t, col, km_t, vm_t, o, o_layout, wo
                                                    o_layout), ws, ws_bytes, _stream(stream)))
 
 
+def sva_forward(plan: Plan, q, k, v, wq, wk, q_r, k_t, v_t, select_ws, col, km_t, vm_t,
+                attn_ws, o, marks=None, stream=None) -> None:
+    """The whole step in one call (see include/sva.h).  ``marks``: None or
+    SVA_FORWARD_MARKS torch.cuda.Event objects, recorded at the stage
+    boundaries; an event torch has not created yet is recorded once on the
+    stream first, which creates it."""
+    import torch
+    bf = torch.bfloat16
+    shp, wshape = plan.raster_shape, (plan.desc.H, plan.desc.d)
+    sparse, comp = not plan.info.dense, plan.compensated
+    if sparse and (col is None or select_ws is None):
+        raise ValueError("a sparse plan needs col and select_ws")
+    if comp and (km_t is None or vm_t is None):
+        raise ValueError("a compensated plan needs km_t and vm_t")
+    sws, sws_bytes = _workspace(select_ws if sparse else None)
+    aws, aws_bytes = _workspace(attn_ws)
+    b = sva_step_buffers(
+        q=_tensor(q, shp, bf, "q").value, k=_tensor(k, shp, bf, "k").value,
+        v=_tensor(v, shp, bf, "v").value,
+        wq=_tensor(wq, wshape, torch.float32, "wq").value if wq is not None else None,
+        wk=_tensor(wk, wshape, torch.float32, "wk").value if wk is not None else None,
+        q_r=_tensor(q_r, plan.tile_shape, bf, "q_r").value,
+        k_t=_tensor(k_t, plan.kt_shape, bf, "k_t").value,
+        v_t=_tensor(v_t, plan.vt_shape, bf, "v_t").value,
+        select_ws=sws.value if sws is not None else None, select_ws_bytes=sws_bytes,
+        col=_tensor(col, (int(plan.info.nnz),), torch.int32, "col").value if sparse else None,
+        km_t=_tensor(km_t, plan.km_shape, bf, "km_t").value if comp else None,
+        vm_t=_tensor(vm_t, plan.vm_shape, bf, "vm_t").value if comp else None,
+        attn_ws=aws.value if aws is not None else None, attn_ws_bytes=aws_bytes,
+        o=_tensor(o, shp, bf, "o").value)
+    st = _stream(stream)
+    mk = None
+    if marks is not None:
+        if len(marks) != SVA_FORWARD_MARKS:
+            raise ValueError(f"marks must hold {SVA_FORWARD_MARKS} events")
+        handles = []
+        for ev in marks:
+            if ev.cuda_event == 0:
+                ev.record(torch.cuda.current_stream() if stream is None else stream)
+            handles.append(ev.cuda_event)
+        mk = (ctypes.c_void_p * SVA_FORWARD_MARKS)(*handles)
+    _check(lib().sva_forward(plan.handle, ctypes.byref(b), mk, st))
+
+
 def sva_status_string(status: int) -> str:
     return lib().sva_status_string(status).decode()
 
@@ -504,11 +559,18 @@ class Buffers:
         self.aws = torch.empty(aws, dtype=torch.uint8, device=device) if aws else None
 
 
-def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
-    """The whole step, fused where the library allows: the prologue writes Q'
-    in tile order, K' as K tiles and the block means, V is reordered into V
-    tiles, blocks are ranked from those means, and the attention writes O
+def forward(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None, marks=None):
+    """The whole step in one library call (sva_forward): the prologue writes
+    Q' in tile order, K' as K tiles and the block means; V is reordered into
+    V tiles; blocks are ranked from the means; the attention writes O
     straight into raster order.  Returns the raster output tensor ``buf.o``."""
+    sva_forward(plan, q, k, v, wq, wk, buf.q_r, buf.k_t, buf.v_t, buf.ws, buf.col, buf.km_t,
+                buf.vm_t, buf.aws, buf.o, marks, stream)
+    return buf.o
+
+
+def forward_calls(plan: Plan, q, k, v, wq, wk, buf: Buffers, stream=None):
+    """The same fused step as separate library calls."""
     sparse = not plan.info.dense
     sva_qk_norm_rope_tiled(plan, q, k, wq, wk, buf.q_r, buf.k_t,
                            buf.ws if sparse else None, stream)

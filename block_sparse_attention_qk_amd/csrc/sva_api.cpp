@@ -345,6 +345,69 @@ int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
     return sva_attention_ex(plan, q_r, k_t, v_t, col, km_t, vm_t, o_r, SVA_LAYOUT_TILE, stream);
 }
 
+int sva_forward(sva_plan plan, const sva_step_buffers* b, void* const* marks, void* stream) {
+    using sva::aligned16;
+    if (!plan || !b) return set_err(SVA_ERR_INVALID_ARG, "plan or buffers is NULL");
+    const sva_plan_info& I = plan->host.info;
+    const bool sparse = !I.dense;
+    const bool comp = sparse && (plan->host.desc.flags & SVA_COMPENSATE);
+    // every check of the calls below, before anything is enqueued
+    if (!b->q || !b->k || !b->v || !b->q_r || !b->k_t || !b->v_t || !b->o)
+        return set_err(SVA_ERR_INVALID_ARG, "q, k, v, q_r, k_t, v_t and o must be non-NULL");
+    if (!aligned16(b->q) || !aligned16(b->k) || !aligned16(b->v) || !aligned16(b->wq) ||
+        !aligned16(b->wk) || !aligned16(b->q_r) || !aligned16(b->k_t) || !aligned16(b->v_t) ||
+        !aligned16(b->o) || !aligned16(b->select_ws) || !aligned16(b->attn_ws) ||
+        ((uintptr_t)b->col & 3u) || (comp && (!aligned16(b->km_t) || !aligned16(b->vm_t))))
+        return set_err(SVA_ERR_INVALID_ARG, "misaligned pointer");
+    if (b->q_r == b->q || b->q_r == b->k || b->k_t == b->q || b->k_t == b->k || b->v_t == b->v)
+        return set_err(SVA_ERR_INVALID_ARG, "outputs must not alias the inputs");
+    if (sparse) {
+        if (!b->col || !b->select_ws)
+            return set_err(SVA_ERR_INVALID_ARG, "a sparse plan needs col and select_ws");
+        if (b->select_ws_bytes < I.select_workspace_bytes)
+            return set_err(SVA_ERR_WORKSPACE, "select_ws smaller than select_workspace_bytes");
+    }
+    if (comp && (!b->km_t || !b->vm_t))
+        return set_err(SVA_ERR_INVALID_ARG, "a compensated plan needs km_t and vm_t");
+    if (b->attn_ws && I.attention_workspace_bytes > 0 &&
+        b->attn_ws_bytes < I.attention_workspace_bytes)
+        return set_err(SVA_ERR_WORKSPACE, "attn_ws smaller than attention_workspace_bytes");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> hipError_t {
+        return (marks && marks[i]) ? hipEventRecord(static_cast<hipEvent_t>(marks[i]), s)
+                                   : hipSuccess;
+    };
+    hipError_t e = hipSuccess;
+    int rc = SVA_OK;
+#define SVA_MARK(I_)                                                           \
+    do {                                                                       \
+        if ((e = mark(I_)) != hipSuccess) return sva::hip_err(e, "hipEventRecord(mark)"); \
+    } while (0)
+#define SVA_CALL(X_)                                                           \
+    do {                                                                       \
+        if ((rc = (X_)) != SVA_OK) return rc;                                  \
+    } while (0)
+    SVA_MARK(0);
+    SVA_CALL(sva_qk_norm_rope_tiled(plan, b->q, b->k, b->wq, b->wk, b->q_r, b->k_t,
+                                    sparse ? b->select_ws : nullptr, b->select_ws_bytes, stream));
+    SVA_MARK(1);
+    SVA_CALL(sva_reorder(plan, b->v, b->v_t, SVA_FORWARD_VT, stream));
+    SVA_MARK(2);
+    if (sparse)
+        SVA_CALL(sva_select_blocks(plan, nullptr, nullptr, b->select_ws, b->select_ws_bytes,
+                                   b->col, stream));
+    SVA_MARK(3);
+    if (comp) SVA_CALL(sva_block_means(plan, b->k_t, b->v_t, b->km_t, b->vm_t, stream));
+    SVA_MARK(4);
+    SVA_CALL(sva_attention_ws(plan, b->q_r, b->k_t, b->v_t, sparse ? b->col : nullptr,
+                              comp ? b->km_t : nullptr, comp ? b->vm_t : nullptr, b->o,
+                              SVA_LAYOUT_RASTER, b->attn_ws, b->attn_ws_bytes, stream));
+    SVA_MARK(5);
+#undef SVA_CALL
+#undef SVA_MARK
+    return SVA_OK;
+}
+
 const char* sva_status_string(int status) {
     switch (status) {
         case SVA_OK: return "ok";

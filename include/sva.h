@@ -10,6 +10,9 @@
  *                      query block and head
  *   sva_attention      online-softmax attention over the kept blocks only
  *
+ * or in one: sva_forward runs the whole step with the fused variants of
+ * these calls.
+ *
  * Sources of the operations (web pages on the subject):
  *  - "MiniMax-H3 在 8×H200 上基准测试" (SGLang Diffusion benchmark),
  *    section "内核层": QK RMSNorm and 3D RoPE fused in one kernel, with the
@@ -315,6 +318,45 @@ int sva_attention_compensated(sva_plan plan, const void* q_r, const void* k_t,
 int sva_attention_ex(sva_plan plan, const void* q_r, const void* k_t, const void* v_t,
                      const int32_t* col, const void* km_t, const void* vm_t, void* o,
                      int o_layout, void* stream);
+
+/* ---- the whole step ---- */
+
+/* Device buffers of one sva_forward call: caller-owned device memory,
+ * 16-byte aligned (col 4-byte), shapes as for the calls named there. */
+typedef struct {
+    const void* q;           /* raster [B, N, H, d] bf16 inputs                */
+    const void* k;
+    const void* v;
+    const float* wq;         /* [H, d] float32 norm weights, or NULL for ones  */
+    const float* wk;
+    void* q_r;               /* written: Q' in tile order [B, H, Np, d]        */
+    void* k_t;               /* written: K' as K tiles                         */
+    void* v_t;               /* written: V as V tiles                          */
+    void* select_ws;         /* sparse plans: info.select_workspace_bytes      */
+    size_t select_ws_bytes;
+    int32_t* col;            /* sparse plans, written: [nnz] kept block lists  */
+    void* km_t;              /* compensated plans, written: mean tiles; else   */
+    void* vm_t;              /*   NULL                                         */
+    void* attn_ws;           /* optional: info.attention_workspace_bytes, or   */
+    size_t attn_ws_bytes;    /*   NULL (no row split)                          */
+    void* o;                 /* written: O in raster order [B, N, H, d]        */
+} sva_step_buffers;
+
+#define SVA_FORWARD_MARKS 6
+
+/* The whole step in one call, on `stream`: sva_qk_norm_rope_tiled
+ * (writing the block means for a sparse plan), sva_reorder(SVA_FORWARD_VT)
+ * of v, sva_select_blocks from the means (sparse plans),
+ * sva_block_means (compensated plans) and sva_attention_ws with O in
+ * raster order; the results are those of these calls made in this order.
+ * marks: NULL, or SVA_FORWARD_MARKS hipEvent_t created by the caller (NULL
+ * entries skipped), recorded on `stream` at [0] the start and after [1] the
+ * prologue, [2] the V reorder, [3] the selection, [4] the block means and
+ * [5] the attention (an absent stage leaves two marks together), so one
+ * call is timed stage by stage.  Argument errors as for the calls named,
+ * all detected on the host before anything is enqueued. */
+int sva_forward(sva_plan plan, const sva_step_buffers* buffers, void* const* marks,
+                void* stream);
 
 /* ---- measurement ---- */
 

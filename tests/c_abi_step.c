@@ -4,6 +4,9 @@
  * (against include/sva.h and the HIP runtime's C API), runs it on inputs it
  * writes and compares the output with the Python binding's, bit for bit.
  *
+ * The same step is then run as one sva_forward call and must give the same
+ * bytes.
+ *
  * usage: c_abi_step B H T Hh W d block sparsity flags in.bin out.bin
  * in.bin: q, k, v as [B, N, H, d] bf16 (raw), then wq, wk as [H, d] fp32.
  * out.bin: O as [B, N, H, d] bf16. */
@@ -91,6 +94,29 @@ int main(int argc, char** argv) {
     HIP_TRY(hipDeviceSynchronize());
 
     HIP_TRY(hipMemcpy(host, o, raster * 2, hipMemcpyDeviceToHost));
+
+    /* the same step as one sva_forward call, into a second output: the
+     * two must agree bit for bit */
+    void* o2;
+    HIP_TRY(hipMalloc(&o2, raster * 2));
+    sva_step_buffers sb = {0};
+    sb.q = q; sb.k = k; sb.v = v; sb.wq = wq; sb.wk = wk;
+    sb.q_r = q_r; sb.k_t = k_t; sb.v_t = v_t;
+    sb.select_ws = ws; sb.select_ws_bytes = ws_bytes; sb.col = col;
+    sb.o = o2;
+    SVA_TRY(sva_forward(plan, &sb, NULL, NULL));
+    HIP_TRY(hipDeviceSynchronize());
+    unsigned char* host2 = malloc(raster * 2);
+    if (!host2) return 1;
+    HIP_TRY(hipMemcpy(host2, o2, raster * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < raster * 2; ++i)
+        if (host2[i] != host[i]) {
+            fprintf(stderr, "sva_forward differs from the separate calls at byte %zu\n", i);
+            return 1;
+        }
+    free(host2);
+    hipFree(o2);
+
     f = fopen(argv[11], "wb");
     if (!f || fwrite(host, 1, raster * 2, f) != raster * 2) {
         fprintf(stderr, "cannot write %s\n", argv[11]);

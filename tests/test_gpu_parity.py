@@ -302,7 +302,8 @@ def c_step_exe(tmp_path_factory):
 @pytest.mark.parametrize("name", list(_C_STEP))
 def test_c_program_step(name, c_step_exe, tmp_path):
     """A plain C caller (tests/c_abi_step.c: hipMalloc'd buffers, the fused
-    calls on the default stream) gets the same raster output as the Python
+    calls on the default stream, then the same step as one sva_forward call,
+    which it checks against them) gets the same raster output as the Python
     binding's forward(), bit for bit; both use the default tile."""
     wl = _C_STEP[name]
     q, k, v, wq, wk = workload_inputs(wl)
@@ -674,6 +675,45 @@ def test_concurrent_streams(name):
     torch.cuda.synchronize()
     for b, want in zip(bufs, alone):
         assert torch.equal(b.o.view(torch.int16), want)
+
+
+@pytest.mark.parametrize("name", ["ragged128", "dense128", "comp128", "sub64x4", "split128"])
+def test_forward_one_call(name):
+    """sva_forward, the whole step in one call: its output, block lists and
+    V tiles equal those of the same calls made separately, bit for bit, with
+    and without timing marks and on repeated calls; the marks come in stage
+    order; a select workspace that is too small is refused before anything
+    is enqueued."""
+    wl = SPLIT[name] if name in SPLIT else SMALL[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    plan = run.plan
+    x = (run.q, run.k, run.v, run.wq, run.wk)
+    ref = S.Buffers(plan)
+    S.forward_calls(plan, *x, ref)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(S.SVA_FORWARD_MARKS)]
+    for use_marks in (False, True, True):
+        b = S.Buffers(plan)
+        S.forward(plan, *x, b, marks=marks if use_marks else None)
+        torch.cuda.synchronize()
+        assert torch.equal(b.o.view(torch.int16), ref.o.view(torch.int16))
+        assert torch.equal(b.v_t.view(torch.int16), ref.v_t.view(torch.int16))
+        if ref.col is not None:
+            assert torch.equal(b.col, ref.col)
+    t = [marks[0].elapsed_time(m) for m in marks]
+    assert all(b >= a for a, b in zip(t, t[1:])), t
+    if not plan.info.dense:
+        b = S.Buffers(plan)
+        b.o.view(torch.int16).fill_(0x1234)
+        b.col.fill_(-7)
+        small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+        with pytest.raises(S.SvaError) as e:
+            S.sva_forward(plan, *x, b.q_r, b.k_t, b.v_t, small_ws, b.col, b.km_t, b.vm_t, b.aws,
+                          b.o)
+        assert e.value.status == S.SVA_ERR_WORKSPACE
+        torch.cuda.synchronize()
+        assert bool((b.o.view(torch.int16) == 0x1234).all()) and bool((b.col == -7).all())
 
 
 def test_binding_rejects_bad_tensors():
