@@ -26,10 +26,11 @@
 //         order-preserving 64-bit keys (ballot + popcount, no sorting),
 //         takes equal scores lowest index first, and writes the kept
 //         block indices in ascending order with ballot prefix counts.
-//         Mean scorer: float64 fma chains, a thread per key block.  SubBlock
-//         scorer: the run products on the fp64 matrix cores; the terms
-//         exp(x - max) and the final log from the fp32 exponential and log
-//         units, the sum of the terms in float64.  Measured on gfx950, 2^y is
+//         Mean scorer: float64 fma chains, a thread per key block, up to
+//         1024 blocks; beyond that the products on the fp64 matrix cores.
+//         SubBlock scorer: the run products on the fp64 matrix cores; the
+//         terms exp(x - max) and the final log from the fp32 exponential and
+//         log units, the sum of the terms in float64.  Measured on gfx950, 2^y is
 //         within 8.3e-8 relative and log2 within 2.4e-7 absolute on [1, 16],
 //         so a score is within about 4e-7 of its float64 value (scores of
 //         full blocks are several units: log c_a c_b alone is 5.5 for
@@ -189,7 +190,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                                                             const double* kmeanT, int R,
                                                             int32_t* col) {
     constexpr int RT = 8;              // rows per workgroup pass (R <= RT)
-    constexpr int QW = SUBBLOCK ? ((RT * NSUB + 15) / 16) * 16 : RT * NSUB;   // query runs in LDS
+    // products on the matrix cores for the SubBlock scorer, and for the
+    // mean scorer beyond 1024 blocks (below that the fma loop is faster)
+    constexpr bool MFMA = SUBBLOCK || NSLOT > 16;
+    constexpr int QW = MFMA ? ((RT * NSUB + 15) / 16) * 16 : RT * NSUB;   // query runs in LDS
     extern __shared__ double smem[];
     double* qs = smem;                 // [D][QW], rows past nrows zero
     double* sc = smem + QW * D;        // [R][nB]
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     const int qb0 = g * R;
     const int nrows = min(R, nB - qb0);
 
-    if constexpr (!SUBBLOCK) {
+    if constexpr (!MFMA) {
         for (int i = threadIdx.x; i < QW * D; i += kTopkThreads) {
             const int dd = i / QW, ra = i % QW;
             qs[i] = ra / NSUB < nrows ? qmean[((bh * nB + qb0) * NSUB + ra) * D + dd] : 0.0;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     __syncthreads();
 
     const double* kt = kmeanT + bh * D * (int64_t)nB * NSUB;
-    if constexpr (!SUBBLOCK) {
+    if constexpr (!MFMA) {
         // Mean scorer: thread per key block, all RT rows at once (its key
         // means are one 512-byte wave load per channel, the query means a
         // broadcast LDS read); each score is the sequential fma chain over
@@ -253,7 +257,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                 if (r < nrows) sc[r * nB + kb] = acc[r];
         }
     } else {
-        // SubBlock scorer on the fp64 matrix cores: the score tile of 16
+        // Products on the fp64 matrix cores (runs are whole blocks for the
+        // mean scorer): the score tile of 16
         // query runs x 16 key runs is a sum of D/4 v_mfma_f64_16x16x4f64
         // (A = query means, 16 runs x 4 channels; B = key means, 4 channels
         // x 16 runs).  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
@@ -264,8 +269,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
         // in NSUB neighbouring lanes.  The query operands were staged in
         // LDS in lane order (one conflict-free 8-byte read per lane and
         // MFMA); each wave streams 16-run key tiles from the transposed key
-        // means, the next tile loading while the current one is multiplied,
-        // and finishes
+        // means, the next tile loading while the current one is multiplied.
+        // The mean scorer's score is the product itself; the SubBlock scorer
+        // finishes
         //   log sum_a sum_b c_a c_b exp(qbar_a . kbar_b / sqrt(d))
         // with the NSUB x NSUB terms spread over NSUB lanes and registers.
         constexpr int MT = (RT * NSUB + 15) / 16;
@@ -282,18 +288,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
             for (int i = 0; i < 4; ++i) {
                 const int j = mt * 16 + 4 * g4 + i;
                 const int row = j / NSUB;
-                lq[mt][i] = row < nrows ? lgt[run_count(p, qb0 + row, j % NSUB)] : 0.0;
+                lq[mt][i] = SUBBLOCK && row < nrows ? lgt[run_count(p, qb0 + row, j % NSUB)] : 0.0;
             }
         // key means of this (b, h) through a buffer resource: per-lane byte
         // offset of (channel l / 16, run), plus a scalar offset per 4-channel step
         const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)kt, (short)0, D * nks * (int)sizeof(double), 0x00020000);
-        // the valid count of the lane's key block is loaded first, with the
-        // tile's key means (loads complete in order: a later global read
-        // would wait for the whole prefetch)
+        // the valid count of the lane's key block (SubBlock) is loaded first,
+        // with the tile's key means (loads complete in order: a later global
+        // read would wait for the whole prefetch)
         auto load_tile = [&](double (&b)[KS], int& nval, int t) {
             const int ksc = min(t * 16 + n16, nks - 1);
-            nval = p.blk_valid[ksc / NSUB];
+            nval = SUBBLOCK ? p.blk_valid[ksc / NSUB] : 0;
             const int voff = (g4 * nks + ksc) * (int)sizeof(double);
 #pragma unroll
             for (int s = 0; s < KS; ++s)
@@ -313,6 +319,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                                                                  c[mt], 0, 0, 0);
             const int ks = t * 16 + n16;
             const int kb = ks / NSUB;
+            if constexpr (!SUBBLOCK) {
+                // lane (l / 16, l % 16) holds query blocks 4(l / 16) + i
+                // against key block kb
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = mt * 16 + 4 * g4 + i;
+                        if (row < nrows && kb < nB) sc[row * nB + kb] = c[mt][i];
+                    }
+                return;
+            }
             const double lk = lgt[min(max(nval - (ks % NSUB) * sb, 0), sb)];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -473,7 +491,8 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     }
     // rows per workgroup: up to 8, as many as the score rows' LDS allows
     // next to the query runs (8 rows × nsub runs × d)
-    const int qruns = p.scorer == 0 ? 8 : (8 * p.nsub + 15) / 16 * 16;
+    const int nslot = (p.nB + 63) / 64;
+    const int qruns = p.scorer == 0 && nslot <= 16 ? 8 : (8 * p.nsub + 15) / 16 * 16;
     const int qbytes = qruns * p.d * (int)sizeof(double);
     int R = (kScoreLds - qbytes) / (p.nB * (int)sizeof(double));
     R = R < 1 ? 1 : (R > 8 ? 8 : R);
@@ -481,7 +500,6 @@ hipError_t launch_select(const DevPlan& p, const uint16_t* qr, const uint16_t* k
     dim3 grid((unsigned)(BH * groups));
     const size_t lds = (size_t)qbytes + (size_t)R * p.nB * sizeof(double) +
                        (size_t)(p.block + 1) * sizeof(double);
-    const int nslot = (p.nB + 63) / 64;
 #define SVA_TOPK(DD, NS, NSB, SBK)                                                           \
     hipLaunchKernelGGL((topk_kernel<DD, NS, NSB, SBK>), grid, dim3(kTopkThreads), lds, s, p,  \
                        qmean, kmeanT, R, col)
