@@ -27,7 +27,7 @@ import torch
 import block_sparse_attention_qk_amd as S
 from block_sparse_attention_qk_amd import inputs as I
 import oracle.sva_oracle as O
-from _parity import (MAX_ABS, REL_L2, GpuRun, chain_flips, compare_masks, dev, geometry, host,
+from _parity import (MAX_ABS, REL_L2, TIE_MARGIN, GpuRun, chain_flips, compare_masks, dev, geometry, host,
                      host_f64, kept_from_col, max_abs, oracle_selection, prologue_check, rel_l2,
                      workload_inputs)
 
@@ -219,6 +219,61 @@ def test_select_parity(name):
         excused += e
     print(f"{name}: mask differences {diffs}, excused ties {excused}")
     assert diffs == excused
+
+
+def test_subblock_near_ties():
+    """The SubBlock ranking where the fp32 screen cannot order the keys at a
+    row's cut: every key block is a copy of one block with one token nudged,
+    so the estimates at a cut differ by a few 1e-6 of the score (median),
+    less than the fp32 scores resolve (about 1e-5) and far more than float64
+    rounding.  Those keys are decided by their float64 re-scores: the kept
+    sets equal the oracle's exactly, with no excused ties."""
+    wl = I.custom("nearties", 1, 2, 4, 16, 16, 128, 64, 0.5, tile=(4, 4, 4), seed_base=13100,
+                  scorer=1, subblocks=4)
+    g = geometry(wl)
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    rng = np.random.default_rng(13101)
+    qr = np.zeros((wl.B, wl.H, g.Np, g.d), np.uint16)
+    kr = np.zeros((wl.B, wl.H, g.Np, g.d), np.uint16)
+    gaps = []
+    for h in range(wl.H):
+        qv = rng.standard_normal((g.Np, g.d))
+        base = rng.standard_normal((g.block, g.d))
+        kv = np.tile(base, (g.nB, 1))
+        for kb in range(g.nB):          # block kb: token kb % block, channel kb % d nudged
+            kv[kb * g.block + kb % g.block, kb % g.d] += 0.3 * (kb + 1)
+        qr[0, h] = O.f64_to_bf16_bits(qv)
+        kr[0, h] = O.f64_to_bf16_bits(kv)
+        kept, scores, thresh, smax = oracle_selection(O.bf16_bits_to_f64(qr[0, h]),
+                                                      O.bf16_bits_to_f64(kr[0, h]), g, meta)
+        for qb in range(g.nB):
+            srt = np.sort(scores[qb])[::-1]
+            k_ = int(kept[qb].sum())
+            gaps.append((srt[k_ - 1] - srt[k_]) / smax[qb])
+    gaps = np.array(gaps)
+    # precondition: most cuts closer than the fp32 screen resolves (about
+    # 1e-5 of the score), typically beyond the tie margin
+    assert 2 * TIE_MARGIN < np.median(gaps) < 1e-5, gaps
+    plan = S.sva_plan_create_ex(S.desc_for(wl))
+    buf = S.Buffers(plan)
+    kt = np.stack([_kt_from_kr(kr[0, h], g) for h in range(wl.H)])[None]
+    S.sva_select_blocks(plan, dev(qr), dev(np.ascontiguousarray(kt)), buf.ws, buf.col)
+    torch.cuda.synchronize()
+    col = buf.col.cpu().numpy()
+    _, row_ptr, _ = plan.host_tables()
+    forced, _ = O.forced_blocks(g, meta)
+    nnz = int(plan.info.nnz_per_head)
+    diffs = excused = 0
+    for h in range(wl.H):
+        ref = oracle_selection(O.bf16_bits_to_f64(qr[0, h]), O.bf16_bits_to_f64(kr[0, h]), g, meta)
+        kept_g = kept_from_col(col[h * nnz:(h + 1) * nnz], row_ptr, g.nB)
+        n, e = compare_masks(kept_g, *ref, forced)
+        diffs += n
+        excused += e
+    print(f"near ties: median cut gap {np.median(gaps):.2e}, smallest {gaps.min():.2e}; "
+          f"mask differences {diffs}, excused {excused}")
+    assert diffs == 0 and excused == 0
 
 
 @pytest.mark.parametrize("name", list(SMALL))
