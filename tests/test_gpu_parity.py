@@ -276,6 +276,38 @@ def test_subblock_near_ties():
     assert diffs == 0 and excused == 0
 
 
+def test_subblock_many_blocks():
+    """The SubBlock ranking beyond 2048 blocks (64 key blocks per lane in
+    the search, the kernel's widest form): 2,100 blocks of 64 tokens in four
+    runs, one head, selection from tile-ordered Q', K' against the oracle's
+    ranking of the same values."""
+    wl = I.custom("sub_many", 1, 1, 2, 168, 400, 128, 64, 0.8, tile=(2, 8, 8), seed_base=13200,
+                  scorer=1, subblocks=4)
+    g = geometry(wl)
+    assert g.nB > 2048
+    perm = O.permutation(g)
+    meta = O.block_meta(g, perm)
+    rng = np.random.default_rng(13201)
+    valid = np.zeros(g.Np, bool)
+    valid[perm] = True
+    qv = rng.standard_normal((g.Np, g.d)) * valid[:, None]
+    kv = (rng.standard_normal((g.Np, g.d)) + 0.5 * np.sin(np.arange(g.Np) / 700.0)[:, None]) * valid[:, None]
+    qr = O.f64_to_bf16_bits(qv)
+    kr = O.f64_to_bf16_bits(kv)
+    plan = S.sva_plan_create_ex(S.desc_for(wl))
+    buf = S.Buffers(plan)
+    S.sva_select_blocks(plan, dev(qr[None, None]), dev(_kt_from_kr(kr, g)[None, None]), buf.ws,
+                        buf.col)
+    torch.cuda.synchronize()
+    ref = oracle_selection(O.bf16_bits_to_f64(qr), O.bf16_bits_to_f64(kr), g, meta)
+    _, row_ptr, _ = plan.host_tables()
+    forced, _ = O.forced_blocks(g, meta)
+    kept_g = kept_from_col(buf.col.cpu().numpy(), row_ptr, g.nB)
+    n, e = compare_masks(kept_g, *ref, forced)
+    print(f"sub_many: {g.nB} blocks, mask differences {n}, excused ties {e}")
+    assert n == e
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_attention_parity(name):
     wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
