@@ -466,20 +466,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
     // the `need`-th largest key T (a prefix of it once the kept set is
     // fixed) and how many keys equal to T are kept, by a bitwise search on
     // order-preserving 64-bit keys (0 = not a candidate)
-    auto threshold = [&](const uint64_t (&key)[NSLOT], int need, uint64_t& T, int& need_eq) {
-        uint64_t kmax = 0, kmin = ~0ull;
+    // prefix: start below the bits every key shares (a wave max and min
+    // first).  Dot-product scores take both signs, so their keys differ in
+    // the top bit and the mean scorer starts there; SubBlock estimates
+    // (positive, close together) share many leading bits.
+    auto threshold = [&](const uint64_t (&key)[NSLOT], int need, uint64_t& T, int& need_eq,
+                         bool prefix) {
+        int top = 63;
+        T = 0;
+        if (prefix) {
+            uint64_t kmax = 0, kmin = ~0ull;
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j)
-            if (key[j]) {
-                kmax = key[j] > kmax ? key[j] : kmax;
-                kmin = key[j] < kmin ? key[j] : kmin;
-            }
-        kmax = wave_max_u64(kmax);
-        kmin = wave_min_u64(kmin);
-        const uint64_t diff = kmax ^ kmin;
-        int top = diff ? 63 - __clzll(diff) : -1;
-        T = top >= 0 ? (kmin & ~((2ull << top) - 1)) : kmin;
-        if (top == 63) T = 0;
+            for (int j = 0; j < NSLOT; ++j)
+                if (key[j]) {
+                    kmax = key[j] > kmax ? key[j] : kmax;
+                    kmin = key[j] < kmin ? key[j] : kmin;
+                }
+            kmax = wave_max_u64(kmax);
+            kmin = wave_min_u64(kmin);
+            const uint64_t diff = kmax ^ kmin;
+            top = diff ? 63 - __clzll(diff) : -1;
+            T = top >= 0 ? (kmin & ~((2ull << top) - 1)) : kmin;
+            if (top == 63) T = 0;
+        }
         // largest T with count(key >= T) >= need.  Once a candidate leaves
         // exactly `need` keys at or above it, those are the kept ones and
         // every later candidate keeps the same set, so the search stops
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
         int need_eq = 0;
         uint64_t bbits = 0;                    // SubBlock: slots in the band, kept by rescoring
         if (need > 0) {
-            threshold(key, need, T, need_eq);
+            threshold(key, need, T, need_eq, SUBBLOCK);
             if constexpr (SUBBLOCK) {
                 // The fp32 scores decide every key farther than twice the
                 // row's largest bound from the need-th largest fp32 score
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                 }
                 uint64_t T2 = 0;
                 int need_eq2 = 0;
-                if (need_b > 0 && need_b < n_band) threshold(key2, need_b, T2, need_eq2);
+                if (need_b > 0 && need_b < n_band) threshold(key2, need_b, T2, need_eq2, true);
                 // band keys kept: key2 > T2, or equal to T2 in index order
                 int eq_seen = 0;
                 uint64_t kbits = 0;
