@@ -803,6 +803,60 @@ def test_forward_one_call(name):
         assert bool((b.o.view(torch.int16) == 0x1234).all()) and bool((b.col == -7).all())
 
 
+_GUARD = 1 << 16   # guard bytes on each side of a buffer
+_CANARY = 0xA5
+
+
+class _Guarded:
+    """Every buffer of S.Buffers(plan), each placed between two 64 KB guard
+    regions filled with a canary byte (the buffer itself starts filled with
+    it too), so that a write past either end of any output shows."""
+
+    def __init__(self, plan):
+        self.raw = {}
+        for name, t in vars(S.Buffers(plan)).items():
+            if t is None:
+                setattr(self, name, None)
+                continue
+            nbytes = t.numel() * t.element_size()
+            raw = torch.full((2 * _GUARD + nbytes,), _CANARY, dtype=torch.uint8, device="cuda")
+            setattr(self, name, raw[_GUARD:_GUARD + nbytes].view(t.dtype).view(t.shape))
+            self.raw[name] = (raw, nbytes)
+
+    def untouched_guards(self):
+        """Names of the buffers whose guard bytes changed."""
+        bad = []
+        for name, (raw, nbytes) in self.raw.items():
+            if not (bool((raw[:_GUARD] == _CANARY).all())
+                    and bool((raw[_GUARD + nbytes:] == _CANARY).all())):
+                bad.append(name)
+        return bad
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "dense128", "comp128", "sub64x4",
+                                  "split128"])
+def test_outputs_stay_in_bounds(name):
+    """Sentinel canaries: the fused step (sva_forward) and the staged step (one
+    call per stage) write nothing outside their output and workspace
+    buffers, and give the same bits with guarded buffers as with plain ones."""
+    wl = SPLIT[name] if name in SPLIT else SMALL[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    plan = run.plan
+    x = (run.q, run.k, run.v, run.wq, run.wk)
+    for step in (S.forward, S.forward_staged):
+        print(f"{name}: {step.__name__}", flush=True)
+        ref = S.Buffers(plan)
+        step(plan, *x, ref)
+        g = _Guarded(plan)
+        step(plan, *x, g)
+        torch.cuda.synchronize()
+        assert g.untouched_guards() == [], step.__name__
+        assert torch.equal(g.o.view(torch.int16), ref.o.view(torch.int16))
+        if ref.col is not None:
+            assert torch.equal(g.col, ref.col)
+
+
 def test_binding_rejects_bad_tensors():
     wl = SMALL["tiny"]
     plan = S.sva_plan_create_ex(S.desc_for(wl))
