@@ -52,6 +52,11 @@ SMALL = {
     "partial96": I.custom("partial96", 1, 2, 4, 8, 24, 128, 128, 0.5,
                           flags=I.KEEP_SAME_FRAME, n_extra=128, seed_base=9700,
                           rope_split=(32, 32, 32)),
+    # narrow RoPE sections: 4, 2 and 2 channels at d = 64, so the first
+    # 8-channel chunk holds pairs of all three axes and the rest are not
+    # rotated; extra tokens
+    "rope3": I.custom("rope3", 1, 2, 5, 11, 13, 64, 64, 0.5, tile=(2, 4, 8), n_extra=64,
+                      seed_base=11200, rope_split=(4, 2, 2)),
     # SubBlock scorer: 4 runs of 32 tokens, budget rounded up to 8 blocks
     "sub128": I.custom("sub128", 1, 2, 5, 16, 24, 128, 128, 0.6, seed_base=9800,
                        scorer=1, budget_multiple=8),
