@@ -362,7 +362,10 @@ def cpu_baseline(wl, q, k, v, wq, wk, info, heads, gpu_ms):
     import oracle.sva_oracle as O
 
     g = O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
-                   sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra)
+                   sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra,
+                   split=wl.rope_split, scorer=wl.scorer, subblocks=wl.subblocks,
+                   budget_multiple=max(1, wl.budget_multiple), theta=wl.theta_resolved,
+                   eps=wl.eps_resolved)
     cores = len(os.sched_getaffinity(0))
     heads = max(1, min(heads, wl.H))
     t0 = time.perf_counter()

@@ -194,7 +194,9 @@ def desc_for(wl) -> sva_plan_desc:
                               rope_split=getattr(wl, "rope_split", (0, 0, 0)),
                               scorer=getattr(wl, "scorer", SVA_SCORER_MEAN),
                               subblocks=getattr(wl, "subblocks", 0),
-                              budget_multiple=getattr(wl, "budget_multiple", 0))
+                              budget_multiple=getattr(wl, "budget_multiple", 0),
+                              rope_theta=getattr(wl, "rope_theta", 0.0),
+                              eps=getattr(wl, "eps", 0.0))
 
 
 # --------------------------------------------------------------------------

@@ -54,6 +54,16 @@ class Workload:
     scorer: int = 0                 # 0 mean of each block, 1 SubBlock estimate
     subblocks: int = 0              # runs per block for the SubBlock scorer (0 = 4)
     budget_multiple: int = 0        # round the budget up to a multiple (0 = 1)
+    rope_theta: float = 0.0         # RoPE base (0 = 10000)
+    eps: float = 0.0                # RMSNorm epsilon (0 = 1e-6)
+
+    @property
+    def theta_resolved(self) -> float:
+        return self.rope_theta if self.rope_theta else 10000.0
+
+    @property
+    def eps_resolved(self) -> float:
+        return self.eps if self.eps else 1e-6
 
     @property
     def n_video(self) -> int:
@@ -205,8 +215,8 @@ def custom(name: str, B: int, H: int, T: int, Hh: int, W: int, d: int, block: in
            sparsity: float, flags: int = 0, tile=(0, 0, 0), n_extra: int = 0,
            temperature: bool = False, seed_base: int = 9000,
            rope_split=(0, 0, 0), scorer: int = 0, subblocks: int = 0,
-           budget_multiple: int = 0) -> Workload:
+           budget_multiple: int = 0, rope_theta: float = 0.0, eps: float = 0.0) -> Workload:
     """An ad-hoc workload (tests use these for small ragged shapes)."""
     return Workload(name, B, H, T, Hh, W, d, block, sparsity, flags, tuple(tile),
                     n_extra, temperature, seed_base, tuple(rope_split), scorer, subblocks,
-                    budget_multiple)
+                    budget_multiple, rope_theta, eps)

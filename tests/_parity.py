@@ -35,7 +35,8 @@ def geometry(wl) -> O.Geometry:
     return O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
                       sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra,
                       split=wl.rope_split, scorer=wl.scorer, subblocks=wl.subblocks,
-                      budget_multiple=max(1, wl.budget_multiple))
+                      budget_multiple=max(1, wl.budget_multiple), theta=wl.theta_resolved,
+                      eps=wl.eps_resolved)
 
 
 def rel_l2(a, ref):

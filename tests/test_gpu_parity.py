@@ -57,6 +57,10 @@ SMALL = {
     # rotated; extra tokens
     "rope3": I.custom("rope3", 1, 2, 5, 11, 13, 64, 64, 0.5, tile=(2, 4, 8), n_extra=64,
                       seed_base=11200, rope_split=(4, 2, 2)),
+    # RoPE base 500 and RMSNorm epsilon 0.05 in place of the defaults
+    # (10000 and 1e-6): the plan's tables and the norm take the caller's
+    "theta_eps": I.custom("theta_eps", 1, 2, 4, 9, 21, 128, 128, 0.5, flags=I.KEEP_SAME_FRAME,
+                          seed_base=11300, rope_theta=500.0, eps=0.05),
     # SubBlock scorer: 4 runs of 32 tokens, budget rounded up to 8 blocks
     "sub128": I.custom("sub128", 1, 2, 5, 16, 24, 128, 128, 0.6, seed_base=9800,
                        scorer=1, budget_multiple=8),
