@@ -354,7 +354,10 @@ typedef struct {
  * prologue, [2] the V reorder, [3] the selection, [4] the block means and
  * [5] the attention (an absent stage leaves two marks together), so one
  * call is timed stage by stage.  Argument errors as for the calls named,
- * all detected on the host before anything is enqueued. */
+ * all detected on the host before anything is enqueued.  The call only
+ * launches kernels (and records the marks): it allocates, clears and
+ * synchronises nothing, so with marks NULL it can be captured into a HIP
+ * graph and replayed, the buffers staying bound to the captured pointers. */
 int sva_forward(sva_plan plan, const sva_step_buffers* buffers, void* const* marks,
                 void* stream);
 

@@ -812,6 +812,45 @@ def test_forward_one_call(name):
         assert bool((b.o.view(torch.int16) == 0x1234).all()) and bool((b.col == -7).all())
 
 
+@pytest.mark.parametrize("name", ["ragged128", "dense128", "comp128", "sub64x4", "split128"])
+def test_forward_in_a_graph(name):
+    """sva_forward captured into a HIP graph (through torch.cuda.CUDAGraph):
+    the compute calls only launch kernels, so the capture holds the whole
+    step.  Each of three replays, with eager work between them that
+    overwrites the outputs, gives the eager result bit for bit."""
+    wl = SPLIT[name] if name in SPLIT else SMALL[name]
+    q, k, v, wq, wk = workload_inputs(wl)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    plan = run.plan
+    x = (run.q, run.k, run.v, run.wq, run.wk)
+    ref = S.Buffers(plan)
+    S.forward(plan, *x, ref)
+    torch.cuda.synchronize()
+    b = S.Buffers(plan)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.forward(plan, *x, b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        S.forward(plan, *x, b)
+    for rep in range(3):
+        b.o.view(torch.int16).fill_(0x1234)
+        b.v_t.view(torch.int16).fill_(0x1234)
+        if b.col is not None:
+            b.col.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.o.view(torch.int16), ref.o.view(torch.int16)), rep
+        assert torch.equal(b.v_t.view(torch.int16), ref.v_t.view(torch.int16)), rep
+        if ref.col is not None:
+            assert torch.equal(b.col, ref.col), rep
+    del graph
+
+
 _GUARD = 1 << 16   # guard bytes on each side of a buffer
 _CANARY = 0xA5
 
