@@ -204,7 +204,8 @@ def main():
     value = attn_flop / (ms_step * 1e-3) / 1e12
     N, Np, nB = int(info.N), int(info.Np), int(info.nB)
     pro_bytes = 4.0 * B * N * H * d * 2
-    sel_bytes = 2.0 * B * H * Np * d * 2 + 2.0 * B * H * nB * d * 8 + 4.0 * nnz
+    nsub = int(info.subblocks)
+    sel_bytes = 2.0 * B * H * Np * d * 2 + 2.0 * B * H * nB * nsub * d * 8 + 4.0 * nnz
     stage_gbs = {
         "prologue": pro_bytes / (stage["prologue"] * 1e-3) / 1e9,
         "reorder_v": (B * H * (N + Np) * d * 2) / (stage["reorder_v"] * 1e-3) / 1e9,
@@ -218,7 +219,7 @@ def main():
         else:
             # the fused path pools inside the prologue; its select reads the
             # block means and writes the block lists
-            rank_bytes = 2.0 * B * H * nB * int(info.subblocks) * d * 8 + 4.0 * nnz
+            rank_bytes = 2.0 * B * H * nB * nsub * d * 8 + 4.0 * nnz
             stage_gbs["select"] = rank_bytes / (stage["select"] * 1e-3) / 1e9
 
     out = {
