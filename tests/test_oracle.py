@@ -77,6 +77,10 @@ def check_rmsnorm():
     # the weight multiplies each channel
     w = rng.uniform(0.5, 2.0, 128)
     np.testing.assert_allclose(O.rms_norm(x, w, eps), y * w, rtol=1e-14)
+    # a large epsilon enters the same closed form
+    big = 0.5
+    np.testing.assert_allclose(np.mean(O.rms_norm(x, np.ones(128), big) ** 2, axis=1),
+                               ms / (ms + big), rtol=1e-12)
 
 
 def test_rmsnorm_closed_forms():
@@ -99,7 +103,12 @@ def check_rope_library():
     from transformers import LlamaConfig
     from transformers.models.llama.modeling_llama import (LlamaRotaryEmbedding,
                                                           apply_rotary_pos_emb)
-    g = _geom(T=5, Hh=7, W=9, d=64, split=(16, 24, 24), theta=10000.0)
+    for theta in (10000.0, 500.0):
+        _rope_library_case(_geom(T=5, Hh=7, W=9, d=64, split=(16, 24, 24), theta=theta),
+                           LlamaConfig, LlamaRotaryEmbedding, apply_rotary_pos_emb)
+
+
+def _rope_library_case(g, LlamaConfig, LlamaRotaryEmbedding, apply_rotary_pos_emb):
     rng = np.random.default_rng(3)
     x = rng.standard_normal((g.N, g.d))
     y = O.rope_3d(x, g)
@@ -753,10 +762,18 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "rope_angles", bad_angles)
     assert _fails(check_rope_library)
     monkeypatch.setattr(O, "rope_angles", orig_angles)
+    # 2b. RoPE base ignored (always 10000)
+    monkeypatch.setattr(O, "rope_angles", lambda p, w, th: orig_angles(p, w, 10000.0))
+    assert _fails(check_rope_library)
+    monkeypatch.setattr(O, "rope_angles", orig_angles)
     # 3. RMSNorm without the mean (sum of squares)
     orig_norm = O.rms_norm
     monkeypatch.setattr(O, "rms_norm", lambda x, w, eps: np.asarray(x) / np.sqrt(
         np.sum(np.asarray(x) ** 2, axis=-1, keepdims=True) + eps) * w)
+    assert _fails(check_rmsnorm)
+    monkeypatch.setattr(O, "rms_norm", orig_norm)
+    # 3b. RMSNorm epsilon ignored
+    monkeypatch.setattr(O, "rms_norm", lambda x, w, eps: orig_norm(x, w, 0.0))
     assert _fails(check_rmsnorm)
     monkeypatch.setattr(O, "rms_norm", orig_norm)
     # 4. bf16 rounding by truncation
