@@ -196,6 +196,25 @@ def test_prologue_rounding_points():
     assert np.all(np.abs(y - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)
 
 
+def check_prologue_rounding_golden():
+    """The hand-worked case of tests/golden/prologue_rounding_1x1x2.txt: the
+    norm is rounded to bf16 before the rotation and the result after it."""
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "prologue_rounding_1x1x2.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    g = O.Geometry(B=1, H=1, T=1, Hh=1, W=2, d=2, block=64, sparsity=0.0, split=(0, 0, 2),
+                   eps=1e-6, tile=(1, 1, 2))
+    x = np.array([[1.0, 0.0], [1.0, 0.0]])
+    w = np.array([(1.0 + 2.0 ** -8 + 2.0 ** -12) / math.sqrt(2.0), 1.0])
+    y = O.qk_norm_rope(x, w, g)
+    for r in rows:
+        n = int(r[0])
+        np.testing.assert_array_equal(y[n], [float(r[1]), float(r[2])])
+
+
+def test_prologue_rounding_golden():
+    check_prologue_rounding_golden()
+
+
 # ---------------------------------------------------------------- permutation
 
 def check_perm_golden():
@@ -776,6 +795,12 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "rms_norm", lambda x, w, eps: orig_norm(x, w, 0.0))
     assert _fails(check_rmsnorm)
     monkeypatch.setattr(O, "rms_norm", orig_norm)
+    # 3c. no rounding between the norm and the rotation
+    orig_pro = O.qk_norm_rope
+    monkeypatch.setattr(O, "qk_norm_rope", lambda x, w, g: O.to_bf16(
+        O.rope_3d(O.rms_norm(x, w, g.eps), g)))
+    assert _fails(check_prologue_rounding_golden)
+    monkeypatch.setattr(O, "qk_norm_rope", orig_pro)
     # 4. bf16 rounding by truncation
     orig_bf = O.to_bf16
     def trunc(x):
