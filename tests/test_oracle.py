@@ -173,6 +173,24 @@ def test_rope_invariants():
     check_rope_invariants()
 
 
+def check_rope_coordinates():
+    """Each section turns by its own axis coordinate of the raster token
+    n = (t·Hh + h)·W + w: on a 2×3×4 grid with one pair per section (angle =
+    coordinate, frequency theta^0), the pairs (1, 0) of token 23 = (1, 2, 3)
+    come out as (cos c, sin c) for c = 1, 2, 3, and those of token 6 =
+    (0, 1, 2) for c = 0, 1, 2."""
+    g = _geom(T=2, Hh=3, W=4, d=6, split=(2, 2, 2), tile=(1, 1, 4))
+    x = np.tile([1.0, 0.0], (g.N, 3))
+    y = O.rope_3d(x, g)
+    for n, coords in ((23, (1, 2, 3)), (6, (0, 1, 2))):
+        want = np.concatenate([[math.cos(c), math.sin(c)] for c in coords])
+        np.testing.assert_allclose(y[n], want, rtol=0, atol=1e-15)
+
+
+def test_rope_coordinates():
+    check_rope_coordinates()
+
+
 def test_rope_leaves_extra_tokens_and_tail_dims():
     g = _geom(T=2, Hh=4, W=4, d=64, split=(16, 16, 16), n_extra=64)
     rng = np.random.default_rng(5)
@@ -785,6 +803,15 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "rope_angles", lambda p, w, th: orig_angles(p, w, 10000.0))
     assert _fails(check_rope_library)
     monkeypatch.setattr(O, "rope_angles", orig_angles)
+    # 2c. grid coordinates with h and w swapped
+    orig_pos = O.token_positions
+    def swapped(g):
+        t, h, w = orig_pos(g)
+        n = np.arange(g.n_video)
+        return t, n % g.Hh, (n // g.Hh) % g.W
+    monkeypatch.setattr(O, "token_positions", swapped)
+    assert _fails(check_rope_coordinates)
+    monkeypatch.setattr(O, "token_positions", orig_pos)
     # 3. RMSNorm without the mean (sum of squares)
     orig_norm = O.rms_norm
     monkeypatch.setattr(O, "rms_norm", lambda x, w, eps: np.asarray(x) / np.sqrt(
