@@ -355,6 +355,8 @@ def test_selection_properties():
     assert np.array_equal(kept.sum(axis=1), lens)
     assert np.all(kept[forced])                                  # F ⊆ kept
     assert np.all(kept[dense_row])                               # dense rows
+    assert np.all(kept[g.nB_video:])                             # extra-token rows keep all
+    assert dense_row[g.nB_video:].all() and not dense_row[: g.nB_video].any()
     assert np.all(kept[:, g.nB_video:])                          # dense columns
     # sparsity 0 keeps everything
     g0 = O.Geometry(B=1, H=1, T=4, Hh=8, W=16, d=64, block=64, sparsity=0.0, tile=(2, 4, 8))
