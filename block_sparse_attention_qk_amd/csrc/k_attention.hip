@@ -21,10 +21,11 @@
 // They are copied into LDS as they are, with global_load_lds_dwordx4 (each
 // wave-level load moves 1 KB, lane l to byte 16 l), into rotating K and V
 // buffers (four of each with 128-token blocks, three and two with 64): the
-// copies for later stages are issued before a stage is computed, and an
-// iteration ends by waiting only for the stages the next iteration reads
-// (vmcnt; later copies stay in flight) and one barrier.  Per stage each wave
-// computes
+// copies for later stages are issued before a stage is computed; with
+// 64-token blocks an iteration ends by waiting only for the stages the next
+// iteration reads (vmcnt; later copies stay in flight) and one barrier,
+// with 128-token blocks every second iteration waits for its copies and
+// ends with a barrier.  Per stage each wave computes
 //   S^T = K · Q^T    v_mfma_f32_32x32x16_bf16, M = keys, N = queries; the
 //                    operand of lane l for channel step s is the 16 bytes at
 //                    (s·64 + l)·16 of the K stage
@@ -170,12 +171,25 @@ constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // stage st-1 are read in iteration st, so with K copies at least one
 // iteration ahead of their use K needs three buffers, and V two (a stage's
 // V copied in its own iteration, read in the next).  With 128-token
-// blocks: four of each (copies up to three stages ahead; two workgroups of
-// four waves fill a CU's registers).  With 64-token blocks a workgroup has
+// blocks: four of each (two workgroups of four waves fill a CU's
+// registers).  With 64-token blocks a workgroup has
 // only two waves: three K and two V buffers (40 KB at d = 128) let four
 // workgroups, the register limit, share a CU (three with 48 KB).
 constexpr int attn_k_buffers(int, int blk) { return blk == 64 ? 3 : 4; }
 constexpr int attn_v_buffers(int, int blk) { return blk == 64 ? 2 : 4; }
+// Workgroup barrier every BP stages.  With 128-token blocks, one barrier
+// per two stages (K copies three stages ahead, V copies one, every copy
+// landed at each barrier) keeps the four K and four V buffers safe: a wave
+// starting iteration i knows every wave has finished iteration i-2 (odd
+// i) or i-1 (even i), and the buffers a copy overwrites were last read in
+// iteration i-2 or earlier.  Measured against a barrier per stage
+// (bit-identical output): 720p 24.70 -> 24.55 ms, dense HunyuanVideo
+// 143.1 -> 140.7 ms.  The barrier costs little either way (none at all,
+// with wrong results, 24.03 ms); five K buffers with the K copies of the
+// last iteration left in flight were slower (24.68 ms).  64-token blocks
+// keep one barrier per stage: the same scheme needs eight buffers there,
+// which would cost a workgroup per CU.
+constexpr int attn_barrier_period(int, int blk) { return blk == 64 ? 1 : 2; }
 constexpr int attn_gcd(int a, int b) { return b == 0 ? a : attn_gcd(b, a % b); }
 // waves per SIMD the register budget is sized for (LDS decides the rest):
 // two, i.e. at most 256 registers.  Allowed more, the 64-token-block kernel
@@ -205,14 +219,23 @@ void attn_kernel(AttnArgs a) {
     constexpr int NBK = attn_k_buffers(D, BLK);   // K copies run NBK-1 stages ahead
     constexpr int NBV = attn_v_buffers(D, BLK);   // V copies run NBV-1 stages ahead
     static_assert(NBK >= 3 && NBV >= 2 && NBV <= NBK, "stage buffers");
-    constexpr int NU = NBK / attn_gcd(NBK, NBV) * NBV;   // loop unrolling: buffer indices constant
-    static_assert(NU % SPB == 0, "a loop body covers whole blocks");
+    constexpr int BP = attn_barrier_period(D, BLK);
+    static_assert(BP == 1 || BP == 2, "barrier period");
+    // stages the K and V copies run ahead of the iteration that issues them
+    constexpr int KLEAD = NBK - 1;
+    constexpr int VLEAD = BP == 1 ? NBV - 2 : 1;
+    static_assert(BP == 1 || (NBK == 4 && NBV == 4), "buffer schedule of the two-stage barrier");
+    constexpr int NU0 = NBK / attn_gcd(NBK, NBV) * NBV;
+    constexpr int NU1 = NU0 / attn_gcd(NU0, SPB) * SPB;
+    constexpr int NU = NU1 / attn_gcd(NU1, BP) * BP;   // loop unrolling: buffer indices constant
+    static_assert(NU % SPB == 0 && NU % BP == 0, "a loop body covers whole blocks");
     // list entries a loop body touches (its stages and the copies it issues)
-    constexpr int NE = (NU + NBK - 2) / SPB + 1;
-    // At the end of iteration st, K of stage st+2 and V of stage st must
-    // have landed; they were issued in iterations st+3-NBK and st+2-NBV, so
-    // the copies of the min(NBK-3, NBV-2) latest iterations may stay in flight.
-    constexpr int kInFlight = (NBK - 3 < NBV - 2 ? NBK - 3 : NBV - 2) * 2 * LPW;
+    constexpr int NE = (NU - 1 + KLEAD) / SPB + 1;
+    // At each barrier, K of stage st+2 and V of stage st must have landed.
+    // One barrier per stage: they were issued in iterations st+3-NBK and
+    // st+2-NBV, so the copies of the min(NBK-3, NBV-2) latest iterations
+    // may stay in flight.  One per two stages: every copy lands first.
+    constexpr int kInFlight = BP == 1 ? (NBK - 3 < NBV - 2 ? NBK - 3 : NBV - 2) * 2 * LPW : 0;
     static_assert(kInFlight < 64, "vmcnt range");
     constexpr int kWaitNext = (kInFlight & 15) | ((kInFlight >> 4) << 14) | (0x7 << 4) | (0xF << 8);
     __shared__ u32x4_t sK[NBK][CPS];
@@ -488,9 +511,9 @@ void attn_kernel(AttnArgs a) {
     // after the product of stage st-1 in program order, which was taken
     // against the old max.)  The first iteration's product reads a zeroed
     // V buffer with P = 0; the last stage's product follows the loop.
-    // K copies run NBK-1 and V copies NBV-2 stages ahead; at the end of
-    // iteration st, K of stage st+2 and V of stage st (both read in
-    // iteration st+1) have landed.  The loop has no ordinary LDS stores,
+    // K copies run KLEAD and V copies VLEAD stages ahead; at each barrier,
+    // the K and V stages the iterations up to the next barrier read have
+    // landed.  The loop has no ordinary LDS stores,
     // only copies: after this wave's wait, a bare s_barrier makes every
     // wave's part visible and orders every wave's reads of the oldest
     // buffers before the copies into them.  (__syncthreads() would add a
@@ -512,9 +535,9 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) E[e] = e < NC ? C[e] : entry(e);
 #pragma unroll
-        for (int u = 0; u < NBK - 1; ++u) SVA_COPY_K(kb8 + E[u / SPB].off, u % SPB, u);
+        for (int u = 0; u < KLEAD; ++u) SVA_COPY_K(kb8 + E[u / SPB].off, u % SPB, u);
 #pragma unroll
-        for (int u = 0; u < NBV - 2; ++u) SVA_COPY_V(vb8 + E[u / SPB].off, u % SPB, u);
+        for (int u = 0; u < VLEAD; ++u) SVA_COPY_V(vb8 + E[u / SPB].off, u % SPB, u);
         // the V buffer the first iteration's product reads (with P = 0)
         for (int i = tid; i < CPS; i += NT) sV[NBV - 1][i] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -526,6 +549,9 @@ void attn_kernel(AttnArgs a) {
         SVA_MASK(E[0].nv, sc, mx);
         mx = lane_swap_max(mx) * c;
         SVA_RESCALE(mx);
+        // with a barrier every second stage, iteration 1 may copy into the
+        // buffer this first score read: every wave finishes reading it first
+        if (BP == 2) __builtin_amdgcn_s_barrier();
     }
     // A body covers NUE whole list entries (NU stages, a multiple of NBK,
     // NBV and SPB, so every buffer index is a constant).  It needs the
@@ -541,7 +567,7 @@ void attn_kernel(AttnArgs a) {
         for (int u = 0; u < NU; ++u) {
             // a body's later entries may lie past the end of the row
             if (u > 0 && u % SPB == 0 && w + u / SPB >= len) break;
-            const int ck = u + NBK - 1, cv = u + NBV - 2, cs = u + 1;
+            const int ck = u + KLEAD, cv = u + VLEAD, cs = u + 1;
             SVA_COPY_K(kb8 + E[ck / SPB].off, ck % SPB, ck % NBK);
             SVA_COPY_V(vb8 + E[cv / SPB].off, cv % SPB, cv % NBV);
             const int lim = E[cs / SPB].nv - (cs % SPB) * SK;
@@ -552,8 +578,12 @@ void attn_kernel(AttnArgs a) {
             SVA_EXP_CHECKED(sc, pb);
             SVA_MASK_ONLY(lim, sn);
             sc = sn;
-            __builtin_amdgcn_s_waitcnt(kWaitNext);
-            __builtin_amdgcn_s_barrier();
+            // (a body starts at a multiple of BP stages, so u & 1 is the
+            // stage's parity)
+            if (BP == 1 || (u & 1)) {
+                __builtin_amdgcn_s_waitcnt(kWaitNext);
+                __builtin_amdgcn_s_barrier();
+            }
         }
     }
     // the last stage's product (its V landed before the loop's last barrier)
