@@ -577,6 +577,11 @@ void attn_kernel(AttnArgs a) {
             SVA_PV(sV[(u + NBV - 1) % NBV], pb);
             SVA_EXP_CHECKED(sc, pb);
             SVA_MASK_ONLY(lim, sn);
+            // the compiler's small-GEMM interleave of LDS reads and matrix
+            // instructions for this region (bit-identical; 720p 24.60 ->
+            // 24.43 ms, sparse 480p 1.62 -> 1.57 ms, dense HunyuanVideo
+            // 137.8 -> 134.7 ms; its exp-interleave strategies were slower)
+            __builtin_amdgcn_iglp_opt(0);
             sc = sn;
             // (a body starts at a multiple of BP stages, so u & 1 is the
             // stage's parity)
