@@ -18,6 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsva.so")
+# the same library built with device-side index checks (-DSVA_DEBUG); load it
+# by pointing LIB_PATH here before the first call
+DEBUG_LIB_PATH = os.path.join(_HERE, "libsva_debug.so")
 
 SVA_OK = 0
 SVA_ERR_INVALID_ARG = -1
@@ -46,8 +49,13 @@ EXPORTED = (
     "sva_qk_norm_rope", "sva_reorder", "sva_select_blocks", "sva_attention",
     "sva_block_means", "sva_attention_compensated", "sva_qk_norm_rope_tiled",
     "sva_attention_ex", "sva_attention_ws", "sva_select_blocks_noalloc", "sva_stream_copy",
-    "sva_forward", "sva_status_string", "sva_last_error",
+    "sva_forward", "sva_debug_flags", "sva_debug_selftest", "sva_status_string", "sva_last_error",
 )
+
+SVA_DEBUG_TOKEN = 1
+SVA_DEBUG_LIST = 2
+SVA_DEBUG_ROW = 4
+SVA_DEBUG_SELF = 8
 
 SVA_FORWARD_MARKS = 6
 
@@ -126,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.sva_attention_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.sva_attention_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, vp, sz, vp]
     L.sva_forward.argtypes = [vp, P(sva_step_buffers), vp, vp]
+    L.sva_debug_flags.argtypes = [vp, P(u)]
+    L.sva_debug_selftest.argtypes = [vp, vp]
     L.sva_status_string.argtypes = [i]
     L.sva_status_string.restype = ctypes.c_char_p
     L.sva_last_error.argtypes = []
@@ -391,6 +401,21 @@ def sva_select_blocks_noalloc(plan: Plan, q_r, k_t, col, stream=None) -> None:
         plan.handle, _tensor(q_r, plan.tile_shape, torch.bfloat16, "q_r"),
         _tensor(k_t, plan.kt_shape, torch.bfloat16, "k_t"),
         _tensor(col, (int(plan.info.nnz),), torch.int32, "col"), _stream(stream)))
+
+
+def sva_debug_flags(plan: Plan) -> int:
+    """Waits for the device, returns the plan's debug word (SVA_DEBUG_*
+    bits) and clears it.  Raises SvaError (SVA_ERR_UNSUPPORTED) with a
+    release library."""
+    flags = ctypes.c_uint(0)
+    _check(lib().sva_debug_flags(plan.handle, ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def sva_debug_selftest(plan: Plan, stream=None) -> None:
+    """Enqueues the kernel whose check fails on purpose (sets SVA_DEBUG_SELF
+    in a debug library)."""
+    _check(lib().sva_debug_selftest(plan.handle, _stream(stream)))
 
 
 def sva_stream_copy(dst, src, stream=None) -> None:

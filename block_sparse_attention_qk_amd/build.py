@@ -1,9 +1,13 @@
 """Build libsva.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_attention_qk_amd.build
+    python -m block_sparse_attention_qk_amd.build            # libsva.so
+    python -m block_sparse_attention_qk_amd.build --debug    # libsva_debug.so
 
 Every call recompiles every source (the objects go to ``_build/`` next to
-this file, the library to ``libsva.so``).
+this file, the library to ``libsva.so``).  The debug build compiles the same
+sources with -DSVA_DEBUG (device-side index checks reported through the
+plan's debug word, see sva_debug_flags) into ``_build_debug/`` and
+``libsva_debug.so``.
 """
 
 from __future__ import annotations
@@ -19,6 +23,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsva.so")
+DEBUG_OUT_DIR = os.path.join(PKG, "_build_debug")
+DEBUG_LIB = os.path.join(PKG, "libsva_debug.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,9 +46,10 @@ EXTRA = {
 }
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(DEBUG_OUT_DIR if debug else OUT_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *(["-DSVA_DEBUG"] if debug else []),
+           *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,22 +64,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    out_dir, lib = (DEBUG_OUT_DIR, DEBUG_LIB) if debug else (OUT_DIR, LIB)
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, debug), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, debug="--debug" in sys.argv[1:])
     sys.exit(0)

@@ -280,6 +280,7 @@ void attn_kernel(AttnArgs a) {
     const bool q_ok = qfirst + wave_u / WPB < p.nB;
     const int qb = __builtin_amdgcn_readfirstlane(q_ok ? qfirst + wave_u / WPB : p.nB - 1);
     const int qrow = (wave % WPB) * 32 + j;   // query row within the block
+    SVA_DCHECK(p, qfirst >= 0 && qfirst < p.nB, SVA_DEBUG_ROW);
 
     // Q^T operand: lane (j, hf) holds channels 16s + 8hf .. +8 of row qrow
     bf16x8_t qop[DS];
@@ -305,6 +306,12 @@ void attn_kernel(AttnArgs a) {
     const int full_len = DENSE ? p.nB : (int)(p.row_ptr[qb + 1] - p.row_ptr[qb]);
     const int64_t r0 = p.row_ptr[qb] + e0;
     const int len = e1 >= 0 ? e1 - e0 : full_len;
+    SVA_DCHECK(p, DENSE || (full_len >= 0 && full_len <= p.max_row_len), SVA_DEBUG_ROW);
+    // a work item of a split launch: a piece [e0, e1) of the row with a
+    // partial slot, or the whole row with slot -1
+    SVA_DCHECK(p, e1 < 0 || (e0 >= 0 && e0 <= e1 && e1 <= full_len && slot < p.n_slots &&
+                             (slot >= 0 || (e0 == 0 && e1 == full_len))),
+               SVA_DEBUG_ROW);
     const int32_t* cl = DENSE ? nullptr : a.col + bh * p.nnz_per_head + r0;
     // the same list through the constant address space: wave-uniform
     // lookups become scalar loads, which do not count against vmcnt (a
@@ -701,6 +708,7 @@ void attn_kernel(AttnArgs a) {
     if (a.o_raster) {
         if (!row_ok) return;
         const int n = p.inv[qb * BLK + qrow];
+        SVA_DCHECK(p, n >= 0 && n < p.N, SVA_DEBUG_TOKEN);
         const int64_t b = bh / p.H, h = bh - b * p.H;
         op = a.o + ((b * p.N + n) * p.H + h) * (D / 4);
     } else {
@@ -737,6 +745,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DevPlan p, const float*
     const float* base = part + (bh * p.n_slots + s0) * ss;
     const int valid = p.blk_valid[qb];
     const int64_t b = bh / p.H, h = bh - b * p.H;
+    SVA_DCHECK(p, qb >= 0 && qb < p.nB && s0 >= 0 && np >= 1 && s0 + np <= p.n_slots, SVA_DEBUG_ROW);
     for (int idx = threadIdx.x; idx < BLK * C4; idx += 256) {
         const int row = idx / C4, c4 = idx - row * C4;
         float M = -INFINITY;
@@ -763,6 +772,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DevPlan p, const float*
         if (o_raster) {
             if (!row_ok) continue;
             const int n = p.inv[qb * BLK + row];
+            SVA_DCHECK(p, n >= 0 && n < p.N, SVA_DEBUG_TOKEN);
             o[((b * p.N + n) * p.H + h) * C4 + c4] = wv;
         } else {
             o[((bh * p.Np) + (int64_t)qb * BLK + row) * C4 + c4] = wv;

@@ -238,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
     for (int i = 0; i < NP; ++i) {
         const int pos = pos0 + r0 + i * RPP;
         const int n = p.inv[pos < p.Np ? pos : p.Np - 1];
+        SVA_DCHECK(p, pos >= p.Np || (n >= -1 && n < p.N), SVA_DEBUG_TOKEN);
         nr[i] = pos < p.Np ? n : -2;          // -2: past the end, -1: padding
     }
     // this thread's rows (raster offsets of head 0, clamped to a valid row)

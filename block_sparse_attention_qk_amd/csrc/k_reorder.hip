@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kThreads) void reorder_fwd_kernel(DevPlan p, const 
         const uint32_t row = min(row0 + r * RPB, rows - 1);
         bh[r] = fast_div(row, p.div_Np);
         n[r] = p.inv[row - bh[r] * (uint32_t)p.Np];
+        SVA_DCHECK(p, n[r] >= -1 && n[r] < p.N, SVA_DEBUG_TOKEN);
     }
     u32x4 v[kRows];
 #pragma unroll
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const 
         const uint32_t h = row - bn * (uint32_t)p.H;
         const uint32_t b = fast_div(bn, p.div_N);
         pos[r] = p.perm[bn - b * (uint32_t)p.N];
+        SVA_DCHECK(p, pos[r] >= 0 && pos[r] < p.Np, SVA_DEBUG_TOKEN);
         bh[r] = b * (uint32_t)p.H + h;
     }
     u32x4 v[kRows];
@@ -119,7 +121,10 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
     // reads token 0 and is zeroed afterwards)
     int n[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) n[j] = p.inv[kb * BLK + key0 + (j & 3) + 8 * (j >> 2)];
+    for (int j = 0; j < 8; ++j) {
+        n[j] = p.inv[kb * BLK + key0 + (j & 3) + 8 * (j >> 2)];
+        SVA_DCHECK(p, n[j] >= -1 && n[j] < p.N, SVA_DEBUG_TOKEN);
+    }
     u32x4 x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = in[((b * p.N + (n[j] >= 0 ? n[j] : 0)) * p.H + h) * DC + dc];
@@ -179,6 +184,7 @@ __global__ __launch_bounds__(256) void reorder_kt_kernel(DevPlan p, const u32x4*
         const int q = threadIdx.x + i * 256;   // (g, s, hf, j) with j fastest
         const int g = (q >> 6) / (D / 16);
         n[i] = p.inv[kb * BLK + g * 32 + (q & 31)];
+        SVA_DCHECK(p, n[i] >= -1 && n[i] < p.N, SVA_DEBUG_TOKEN);
     }
     u32x4 x[NI];
 #pragma unroll

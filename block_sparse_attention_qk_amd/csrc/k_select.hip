@@ -654,9 +654,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
                     const bool keep = forced || ((hbits | kbits) >> j) & 1ull;
                     const uint64_t km = __ballot(keep);
                     const int slot = base + __popcll(km & lt_mask);
+                    SVA_DCHECK(p, !keep || kb < nB, SVA_DEBUG_LIST);
                     if (keep && slot < len) out[slot] = kb;
                     base += __popcll(km);
                 }
+                SVA_DCHECK(p, base == len, SVA_DEBUG_LIST);
                 continue;
             }
         }
@@ -671,10 +673,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevPlan p, const dou
             const bool keep = forced || (need > 0 && key[j] > T) || (eq && eq_rank < need_eq);
             const uint64_t km = __ballot(keep);
             const int slot = base + __popcll(km & lt_mask);
+            SVA_DCHECK(p, !keep || kb < nB, SVA_DEBUG_LIST);
             if (keep && slot < len) out[slot] = kb;
             base += __popcll(km);
             eq_seen += __popcll(em);
         }
+        SVA_DCHECK(p, base == len, SVA_DEBUG_LIST);
     }
 }
 

@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "sva.h"
+
 namespace sva {
 
 // Exact unsigned division by a plan constant: for 0 <= x < 2^31,
@@ -59,7 +61,26 @@ struct DevPlan {
     int n_items, n_split, n_slots;
     // divisions of (token, head) row indices, all below 2^31
     FastDiv div_H, div_N, div_HW, div_W, div_Np;
+#ifdef SVA_DEBUG
+    uint32_t* dbg;      // the plan's debug word (SVA_DEBUG_* bits)
+#endif
 };
+
+// Debug builds: a failed check ORs its SVA_DEBUG_* bit into the plan's
+// debug word and the kernel goes on.  Release builds compile it away.
+#ifdef SVA_DEBUG
+#define SVA_DCHECK(P, COND, BIT)                                          \
+    do {                                                                  \
+        if (!(COND)) atomicOr((P).dbg, (uint32_t)(BIT));                  \
+    } while (0)
+#else
+#define SVA_DCHECK(P, COND, BIT) \
+    do {                         \
+    } while (0)
+#endif
+
+// debug builds: one kernel whose check fails on purpose (sva_debug_selftest)
+hipError_t launch_debug_selftest(const DevPlan& p, hipStream_t s);
 
 // tiled: qo = Q' in tile order [B,H,Np,d], ko = K' tiles (padding zeroed);
 // otherwise both raster [B,N,H,d].  means (tiled only, may be NULL): the

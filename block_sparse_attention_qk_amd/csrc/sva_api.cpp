@@ -111,7 +111,12 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     const size_t s_blk = align(h.blk_valid.size() * 4), s_rp = align(h.row_ptr.size() * 4);
     const size_t s_rope = align(h.rope_cs.size() * 4);
     const size_t s_items = align(h.items.size() * 4), s_split = align(h.split_rows.size() * 4);
-    const size_t total = s_perm + s_inv + 3 * s_blk + s_rp + s_rope + s_items + s_split;
+#ifdef SVA_DEBUG
+    const size_t s_dbg = 256;   // the debug word
+#else
+    const size_t s_dbg = 0;
+#endif
+    const size_t total = s_perm + s_inv + 3 * s_blk + s_rp + s_rope + s_items + s_split + s_dbg;
     e = hipMalloc(&plan->dmem, total);
     if (e != hipSuccess) {
         delete plan;
@@ -135,6 +140,11 @@ int sva_plan_create_ex(sva_plan* out, const sva_plan_desc* desc) {
     d.rope_cs = static_cast<const float2*>(put(h.rope_cs.data(), h.rope_cs.size() * 4, s_rope));
     d.items = static_cast<const int32_t*>(put(h.items.data(), h.items.size() * 4, s_items));
     d.split_rows = static_cast<const int32_t*>(put(h.split_rows.data(), h.split_rows.size() * 4, s_split));
+#ifdef SVA_DEBUG
+    d.dbg = static_cast<uint32_t*>(static_cast<void*>(base + off));
+    off += s_dbg;
+    if (e == hipSuccess) e = hipMemset(d.dbg, 0, sizeof(uint32_t));
+#endif
     d.n_items = (int)(h.items.size() / 4);
     d.n_split = (int)(h.split_rows.size() / 3);
     d.n_slots = h.n_slots;
@@ -406,6 +416,36 @@ int sva_forward(sva_plan plan, const sva_step_buffers* b, void* const* marks, vo
 #undef SVA_CALL
 #undef SVA_MARK
     return SVA_OK;
+}
+
+int sva_debug_flags(sva_plan plan, unsigned* flags) {
+    if (!plan || !flags) return set_err(SVA_ERR_INVALID_ARG, "plan or flags is NULL");
+    *flags = 0u;
+#ifdef SVA_DEBUG
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return sva::hip_err(e, "hipDeviceSynchronize");
+    uint32_t w = 0;
+    e = hipMemcpy(&w, plan->dev.dbg, sizeof w, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return sva::hip_err(e, "hipMemcpy(debug word)");
+    e = hipMemset(plan->dev.dbg, 0, sizeof w);
+    if (e != hipSuccess) return sva::hip_err(e, "hipMemset(debug word)");
+    *flags = w;
+    return SVA_OK;
+#else
+    return set_err(SVA_ERR_UNSUPPORTED, "release build: the kernels carry no debug checks");
+#endif
+}
+
+int sva_debug_selftest(sva_plan plan, void* stream) {
+    if (!plan) return set_err(SVA_ERR_INVALID_ARG, "plan is NULL");
+#ifdef SVA_DEBUG
+    hipError_t e = sva::launch_debug_selftest(plan->dev, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return sva::hip_err(e, "debug selftest launch");
+    return SVA_OK;
+#else
+    (void)stream;
+    return set_err(SVA_ERR_UNSUPPORTED, "release build: the kernels carry no debug checks");
+#endif
 }
 
 const char* sva_status_string(int status) {

@@ -372,6 +372,32 @@ int sva_forward(sva_plan plan, const sva_step_buffers* buffers, void* const* mar
  * it.  Not part of the attention step. */
 int sva_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* ---- debug build ---- */
+
+/* Built with -DSVA_DEBUG (libsva_debug.so: `python -m
+ * block_sparse_attention_qk_amd.build --debug`), the kernels check the
+ * indices they take from the plan's tables and from the block lists, and the
+ * lists the selection writes.  A failed check sets its bit in the plan's
+ * debug word (a 4-byte device word the plan owns, zero at creation) and the
+ * kernel goes on: nothing traps.  Release builds carry no checks.  Bits: */
+#define SVA_DEBUG_TOKEN 1u  /* a token index from the plan's permutation
+                               tables outside its range */
+#define SVA_DEBUG_LIST 2u   /* a block list row the selection wrote: an entry
+                               outside [0, nB), or not exactly the row length */
+#define SVA_DEBUG_ROW 4u    /* an attention row or work item outside the plan
+                               (query block, row length, split piece, slot) */
+#define SVA_DEBUG_SELF 8u   /* set by sva_debug_selftest */
+
+/* Waits for the device (hipDeviceSynchronize), stores the plan's debug word
+ * in *flags and clears it.  SVA_ERR_UNSUPPORTED in a release build (then
+ * *flags is 0). */
+int sva_debug_flags(sva_plan plan, unsigned* flags);
+
+/* Enqueues on `stream` one kernel whose check fails on purpose, so that the
+ * next sva_debug_flags reports SVA_DEBUG_SELF: a test of the reporting path
+ * itself.  SVA_ERR_UNSUPPORTED in a release build. */
+int sva_debug_selftest(sva_plan plan, void* stream);
+
 /* ---- errors ---- */
 const char* sva_status_string(int status);
 const char* sva_last_error(void);

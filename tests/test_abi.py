@@ -29,6 +29,20 @@ def test_library_exports_every_declared_symbol():
     assert S.sva_status_string(S.SVA_ERR_WORKSPACE) == "workspace too small"
 
 
+def test_debug_library_exports_the_same_symbols():
+    """libsva_debug.so (the same sources built with -DSVA_DEBUG, built
+    beside libsva.so by the package's build) loads and exports every
+    declared symbol; its debug bits match the header's."""
+    assert os.path.exists(S.DEBUG_LIB_PATH), "libsva_debug.so is not built"
+    L = ctypes.CDLL(S.DEBUG_LIB_PATH)
+    for name in S.EXPORTED:
+        assert hasattr(L, name), name
+    header = open(os.path.join(ROOT, "include", "sva.h")).read()
+    bits = dict(re.findall(r"^#define (SVA_DEBUG_\w+) (\d+)u", header, re.M))
+    assert bits == {n: str(getattr(S, n)) for n in
+                    ("SVA_DEBUG_TOKEN", "SVA_DEBUG_LIST", "SVA_DEBUG_ROW", "SVA_DEBUG_SELF")}
+
+
 def _geom(wl):
     return O.Geometry(B=wl.B, H=wl.H, T=wl.T, Hh=wl.Hh, W=wl.W, d=wl.d, block=wl.block,
                       sparsity=wl.sparsity, flags=wl.flags, tile=wl.tile, n_extra=wl.n_extra,
