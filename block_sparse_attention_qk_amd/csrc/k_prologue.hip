@@ -298,113 +298,114 @@ __global__ __launch_bounds__(kThreads) void prologue_tiled_kernel(ProArgs a) {
     }
     const float inv_d = 1.0f / D;
 
-  for (int h = h0; h < h1; ++h) {
-    const int64_t bh = b * p.H + h;
-    if (h > h0 && (KT || mean)) __syncthreads();   // the previous head's LDS reads are done
-    float wv[8];
-    if (w) {
-        const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
-        const float4 w0 = wp[0], w1 = wp[1];
-        wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-    } else {
+    for (int h = h0; h < h1; ++h) {
+        const int64_t bh = b * p.H + h;
+        if (h > h0 && (KT || mean)) __syncthreads();   // the previous head's LDS reads are done
+        float wv[8];
+        if (w) {
+            const float4* wp = reinterpret_cast<const float4*>(w + h * D + sub * 8);
+            const float4 w0 = wp[0], w1 = wp[1];
+            wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+            wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wv[e] = 1.f;
-    }
-    u32x4 x[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) x[i] = in[roff[i] + (int64_t)h * LPR];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) x[i] = nr[i] >= 0 ? x[i] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int r = r0 + i * RPP;
-        const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[2 * e] = bf16lo(u[e]);
-            v[2 * e + 1] = bf16hi(u[e]);
+            for (int e = 0; e < 8; ++e) wv[e] = 1.f;
         }
-        float ss = 0.f;
+        u32x4 x[NP];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+        for (int i = 0; i < NP; ++i) x[i] = in[roff[i] + (int64_t)h * LPR];
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-        u32x4 res = u32x4{0u, 0u, 0u, 0u};
-        if (nr[i] >= 0) {
-            const float rs = rms_scale(ss, inv_d, p.eps);
-            uint32_t ob[4];
+        for (int i = 0; i < NP; ++i) x[i] = nr[i] >= 0 ? x[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int r = r0 + i * RPP;
+            const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+            float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t yb = pack_bf16x2(norm_val(v[2 * e], rs, wv[2 * e]),
-                                                norm_val(v[2 * e + 1], rs, wv[2 * e + 1]));
-                ob[e] = rotate_pair(yb, cs[i][e].x, cs[i][e].y);
+                v[2 * e] = bf16lo(u[e]);
+                v[2 * e + 1] = bf16hi(u[e]);
             }
-            res = u32x4{ob[0], ob[1], ob[2], ob[3]};
-        }
-        if (KT || mean) stage[r * LS + sub] = res;
-        if (!KT && nr[i] != -2) __builtin_nontemporal_store(res, out + (bh * p.Np + pos0 + r) * LPR + sub);
-    }
-    if (!KT && !mean) continue;
-    __syncthreads();
-    if constexpr (KT) {
-        const int g = threadIdx.x >> 6;        // 32-token group of this wave
-        const int lane = threadIdx.x & 63;
-        const int j = lane & 31, hf = lane >> 5;
-        const int gpos = pos0 + g * 32;        // Np is a multiple of 32
-        if (gpos < p.Np) {
-            const int kb = gpos / p.block, t = gpos - kb * p.block;
-            u32x4* dst = out + ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (DS * 64) + lane;
+            float ss = 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < DS; ++s2)
-                __builtin_nontemporal_store(stage[(g * 32 + j) * LS + 2 * s2 + hf], dst + s2 * 64);
+            for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+            for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+            u32x4 res = u32x4{0u, 0u, 0u, 0u};
+            if (nr[i] >= 0) {
+                const float rs = rms_scale(ss, inv_d, p.eps);
+                uint32_t ob[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t yb = pack_bf16x2(norm_val(v[2 * e], rs, wv[2 * e]),
+                                                    norm_val(v[2 * e + 1], rs, wv[2 * e + 1]));
+                    ob[e] = rotate_pair(yb, cs[i][e].x, cs[i][e].y);
+                }
+                res = u32x4{ob[0], ob[1], ob[2], ob[3]};
+            }
+            if (KT || mean) stage[r * LS + sub] = res;
+            if (!KT && nr[i] != -2)
+                __builtin_nontemporal_store(res, out + (bh * p.Np + pos0 + r) * LPR + sub);
         }
-    }
-    if (!mean) continue;
+        if (!KT && !mean) continue;
+        __syncthreads();
+        if constexpr (KT) {
+            const int g = threadIdx.x >> 6;        // 32-token group of this wave
+            const int lane = threadIdx.x & 63;
+            const int j = lane & 31, hf = lane >> 5;
+            const int gpos = pos0 + g * 32;        // Np is a multiple of 32
+            if (gpos < p.Np) {
+                const int kb = gpos / p.block, t = gpos - kb * p.block;
+                u32x4* dst = out + ((bh * p.nB + kb) * (p.block / 32) + (t >> 5)) * (DS * 64) + lane;
+#pragma unroll
+                for (int s2 = 0; s2 < DS; ++s2)
+                    __builtin_nontemporal_store(stage[(g * 32 + j) * LS + 2 * s2 + hf], dst + s2 * 64);
+            }
+        }
+        if (!mean) continue;
 
-    // Pooling.  Thread (slice sl, chunk c) sums 8-channel chunk c over the
-    // slice's SR rows; a run (block/nsub >= 16 rows) is a whole number of
-    // slices.  The slice sums go through LDS (over the staged rows, once
-    // every wave has read them), then one thread per (run, channel) adds
-    // its run's slices.
-    constexpr int NSL = kThreads / LPR;        // slices
-    constexpr int SR = PW / NSL;               // rows per slice (8 or 4)
-    const int sl = threadIdx.x / LPR, c = threadIdx.x % LPR;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        // Pooling.  Thread (slice sl, chunk c) sums 8-channel chunk c over the
+        // slice's SR rows; a run (block/nsub >= 16 rows) is a whole number of
+        // slices.  The slice sums go through LDS (over the staged rows, once
+        // every wave has read them), then one thread per (run, channel) adds
+        // its run's slices.
+        constexpr int NSL = kThreads / LPR;        // slices
+        constexpr int SR = PW / NSL;               // rows per slice (8 or 4)
+        const int sl = threadIdx.x / LPR, c = threadIdx.x % LPR;
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int rr = 0; rr < SR; ++rr) {
-        const u32x4 vv = stage[(sl * SR + rr) * LS + c];
-        const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int rr = 0; rr < SR; ++rr) {
+            const u32x4 vv = stage[(sl * SR + rr) * LS + c];
+            const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += (double)bf16lo(u[e]);
-            acc[2 * e + 1] += (double)bf16hi(u[e]);
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += (double)bf16lo(u[e]);
+                acc[2 * e + 1] += (double)bf16hi(u[e]);
+            }
+        }
+        __syncthreads();
+        double* part = reinterpret_cast<double*>(stage);   // [NSL][D]
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[sl * D + c * 8 + e] = acc[e];
+        __syncthreads();
+        const int RL = p.block / p.nsub;           // rows per run
+        const int spr = RL / SR;                   // slices per run
+        for (int it = threadIdx.x; it < (PW / RL) * D; it += kThreads) {
+            const int run = it / D, ch = it - run * D;
+            const int rpos = pos0 + run * RL;
+            if (rpos >= p.Np) break;
+            double sum = 0.0;
+            for (int k2 = 0; k2 < spr; ++k2) sum += part[(run * spr + k2) * D + ch];
+            const int kb = rpos / p.block;
+            const int rib = (rpos - kb * p.block) / RL;   // run within the block
+            const int valid = min(max(p.blk_valid[kb] - rib * RL, 0), RL);
+            const double m = valid > 0 ? sum / (double)valid : 0.0;
+            if constexpr (KT)
+                mean[(bh * D + ch) * ((int64_t)p.nB * p.nsub) + (int64_t)kb * p.nsub + rib] = m;
+            else
+                mean[((bh * p.nB + kb) * p.nsub + rib) * D + ch] = m;
         }
     }
-    __syncthreads();
-    double* part = reinterpret_cast<double*>(stage);   // [NSL][D]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[sl * D + c * 8 + e] = acc[e];
-    __syncthreads();
-    const int RL = p.block / p.nsub;           // rows per run
-    const int spr = RL / SR;                   // slices per run
-    for (int it = threadIdx.x; it < (PW / RL) * D; it += kThreads) {
-        const int run = it / D, ch = it - run * D;
-        const int rpos = pos0 + run * RL;
-        if (rpos >= p.Np) break;
-        double sum = 0.0;
-        for (int k2 = 0; k2 < spr; ++k2) sum += part[(run * spr + k2) * D + ch];
-        const int kb = rpos / p.block;
-        const int rib = (rpos - kb * p.block) / RL;   // run within the block
-        const int valid = min(max(p.blk_valid[kb] - rib * RL, 0), RL);
-        const double m = valid > 0 ? sum / (double)valid : 0.0;
-        if constexpr (KT)
-            mean[(bh * D + ch) * ((int64_t)p.nB * p.nsub) + (int64_t)kb * p.nsub + rib] = m;
-        else
-            mean[((bh * p.nB + kb) * p.nsub + rib) * D + ch] = m;
-    }
-  }
 }
 
 }  // namespace
