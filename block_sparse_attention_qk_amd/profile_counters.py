@@ -10,7 +10,11 @@ Every counter is summed over the device per dispatch (rocprofv3 reports one
 value per dispatch and counter) and averaged over the dispatches of each
 kernel.  When the LDS counters are present, the table adds two ratios:
 bank-conflict cycles over LDS-active cycles, and cycles waves spent waiting
-for LDS over wave cycles.
+for LDS over wave cycles.  With SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+it adds the matrix units' busy share (busy cycles over the 1024 SIMDs, over
+the graphics-active cycles of the 8 XCDs), and with
+SQ_VALU_MFMA_COEXEC_CYCLES the share of those busy cycles in which vector
+instructions executed beside the matrix instructions.
 """
 
 from __future__ import annotations
@@ -45,8 +49,11 @@ def to_markdown(res: dict, title: str, command: str) -> str:
     counters = sorted({c for cs in res.values() for c in cs})
     lds = {"SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"}
     ratios = lds <= set(counters)
+    mfma = {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(counters)
+    coex = mfma and "SQ_VALU_MFMA_COEXEC_CYCLES" in counters
     head = ["kernel"] + counters + (["bank conflict / LDS active", "LDS wait / wave cycles"]
-                                    if ratios else [])
+                                    if ratios else []) + (["MFMA busy"] if mfma else []) + (
+                                        ["vector co-exec / MFMA busy"] if coex else [])
     lines = [f"# {title}", "", "Command (from the repository root, on the machine with the GPU):", "",
              "```", command, "```", "",
              "Averages per dispatch of each counter, summed over the device.", "",
@@ -58,6 +65,13 @@ def to_markdown(res: dict, title: str, command: str) -> str:
             row.append(f"{cs['SQ_LDS_BANK_CONFLICT'] / act:.3f}" if act > 0 else "—")
             row.append(f"{cs['SQ_WAIT_INST_LDS'] / cs['SQ_WAVE_CYCLES']:.3f}"
                        if cs["SQ_WAVE_CYCLES"] > 0 else "—")
+        if mfma:
+            g = cs["GRBM_GUI_ACTIVE"] / 8
+            busy = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
+            row.append(f"{busy / g * 100:.1f} %" if g > 0 else "—")
+        if coex:
+            b = cs["SQ_VALU_MFMA_BUSY_CYCLES"]
+            row.append(f"{cs['SQ_VALU_MFMA_COEXEC_CYCLES'] / b * 100:.1f} %" if b > 0 else "—")
         lines.append("| " + " | ".join(row) + " |")
     return "\n".join(lines) + "\n"
 
