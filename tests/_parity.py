@@ -185,6 +185,27 @@ def chain_flips(gpu_kept, stage, chain, forced):
     return out
 
 
+def chained_reference(chain, gpu_kept, flips, g, meta):
+    """The chained oracle's tile-ordered output with every query block that
+    has an explained mask flip recomputed by the oracle over the GPU's mask.
+
+    A flip explained by ``chain_flips`` is a boundary tie moved by the
+    prologue's rounding: the GPU's block choice for that row is a correct
+    selection, so the attention it computes must match the oracle's
+    attention over that choice (from the chained oracle's own Q', K', V).
+    Rows without a flip keep the chained oracle's output.  Unexplained flips
+    are left as they are, so they still fail the comparison."""
+    o = chain["o_r"].copy()
+    qbs = sorted({f[0] for f in flips if f[-1]})
+    if qbs:
+        alt = O.block_attention(chain["qr"], chain["kr"], chain["vr"], gpu_kept, g, meta,
+                                qblocks=qbs)
+        for qb in qbs:
+            rows = slice(qb * g.block, (qb + 1) * g.block)
+            o[rows] = alt[rows]
+    return o
+
+
 class GpuRun:
     """The whole step on the GPU with every intermediate kept."""
 
