@@ -42,6 +42,8 @@ SVA_FORWARD = 0
 SVA_INVERSE = 1
 SVA_FORWARD_VT = 2
 SVA_FORWARD_KT = 3
+SVA_ROWS_TO_VT = 4
+SVA_ROWS_TO_KT = 5
 
 EXPORTED = (
     "sva_plan_desc_init", "sva_plan_query", "sva_plan_host_tables",
@@ -369,6 +371,10 @@ def sva_reorder(plan: Plan, inp, out, direction, stream=None) -> None:
         si, so = plan.raster_shape, plan.vt_shape
     elif direction == SVA_FORWARD_KT:
         si, so = plan.raster_shape, plan.kt_shape
+    elif direction == SVA_ROWS_TO_VT:
+        si, so = plan.tile_shape, plan.vt_shape
+    elif direction == SVA_ROWS_TO_KT:
+        si, so = plan.tile_shape, plan.kt_shape
     else:
         raise ValueError("unknown direction")
     _check(lib().sva_reorder(plan.handle, _tensor(inp, si, torch.bfloat16, "in"),

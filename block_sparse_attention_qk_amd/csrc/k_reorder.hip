@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void reorder_inv_kernel(DevPlan p, const 
 // chunk kg (over the whole block) for channel chunk dc (8 rows of 16
 // bytes), turns the 8×8 bf16 square around in registers and writes
 // channels dc*8..dc*8+7 of that chunk (128 contiguous bytes).
-template <int D, int BLK>
+// ROWS: the input is already in tile order [B, H, Np, d] (row bh·Np + pos)
+// instead of raster; padding positions are still written as zeros.
+template <int D, int BLK, bool ROWS>
 __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan p,
                                                                        const u32x4* in,
                                                                        u32x4* out) {
@@ -127,7 +129,9 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
     }
     u32x4 x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = in[((b * p.N + (n[j] >= 0 ? n[j] : 0)) * p.H + h) * DC + dc];
+    for (int j = 0; j < 8; ++j)
+        x[j] = ROWS ? in[(bh * p.Np + kb * BLK + key0 + (j & 3) + 8 * (j >> 2)) * DC + dc]
+                    : in[((b * p.N + (n[j] >= 0 ? n[j] : 0)) * p.H + h) * DC + dc];
     uint32_t m[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -166,7 +170,7 @@ __global__ __launch_bounds__((D / 8) * (BLK / 8)) void reorder_vt_kernel(DevPlan
 // follows the output, so every wave writes 1 KB contiguously and reads 32
 // bytes from each of 32 rows (the rest of those rows is read by the
 // neighbouring waves of the same workgroup, out of the caches).
-template <int D, int BLK>
+template <int D, int BLK, bool ROWS>
 __global__ __launch_bounds__(256) void reorder_kt_kernel(DevPlan p, const u32x4* in,
                                                         u32x4* out) {
     constexpr int DC = D / 8;              // 16-byte chunks per row
@@ -191,7 +195,8 @@ __global__ __launch_bounds__(256) void reorder_kt_kernel(DevPlan p, const u32x4*
     for (int i = 0; i < NI; ++i) {
         const int q = threadIdx.x + i * 256;
         const int hf = (q >> 5) & 1, s = (q >> 6) % (D / 16);
-        x[i] = in[((b * p.N + (n[i] >= 0 ? n[i] : 0)) * p.H + h) * DC + 2 * s + hf];
+        x[i] = ROWS ? in[(bh * p.Np + kb * BLK + ((q >> 6) / (D / 16)) * 32 + (q & 31)) * DC + 2 * s + hf]
+                    : in[((b * p.N + (n[i] >= 0 ? n[i] : 0)) * p.H + h) * DC + 2 * s + hf];
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) dst[threadIdx.x + i * 256] = n[i] >= 0 ? x[i] : u32x4{0u, 0u, 0u, 0u};
@@ -215,27 +220,31 @@ hipError_t launch_reorder(const DevPlan& p, const uint16_t* in, uint16_t* out, i
         dim3 grid((unsigned)((rows + per_block - 1) / per_block));
         if (p.d == 128) hipLaunchKernelGGL(reorder_inv_kernel<128>, grid, dim3(kThreads), 0, s, p, i4, o4);
         else hipLaunchKernelGGL(reorder_inv_kernel<64>, grid, dim3(kThreads), 0, s, p, i4, o4);
-    } else if (direction == 3) {
+    } else if (direction == 3 || direction == 5) {
         dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
+        auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p, i4, o4); };
+        const bool rows = direction == 5;
         if (p.d == 128 && p.block == 128)
-            hipLaunchKernelGGL((reorder_kt_kernel<128, 128>), grid, dim3(256), 0, s, p, i4, o4);
+            rows ? go(reorder_kt_kernel<128, 128, true>) : go(reorder_kt_kernel<128, 128, false>);
         else if (p.d == 128)
-            hipLaunchKernelGGL((reorder_kt_kernel<128, 64>), grid, dim3(256), 0, s, p, i4, o4);
+            rows ? go(reorder_kt_kernel<128, 64, true>) : go(reorder_kt_kernel<128, 64, false>);
         else if (p.block == 128)
-            hipLaunchKernelGGL((reorder_kt_kernel<64, 128>), grid, dim3(256), 0, s, p, i4, o4);
+            rows ? go(reorder_kt_kernel<64, 128, true>) : go(reorder_kt_kernel<64, 128, false>);
         else
-            hipLaunchKernelGGL((reorder_kt_kernel<64, 64>), grid, dim3(256), 0, s, p, i4, o4);
+            rows ? go(reorder_kt_kernel<64, 64, true>) : go(reorder_kt_kernel<64, 64, false>);
     } else {
         dim3 grid((unsigned)((int64_t)p.B * p.H * p.nB));
         const int threads = (p.d / 8) * (p.block / 8);
+        auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(threads), 0, s, p, i4, o4); };
+        const bool rows = direction == 4;
         if (p.d == 128 && p.block == 128)
-            hipLaunchKernelGGL((reorder_vt_kernel<128, 128>), grid, dim3(threads), 0, s, p, i4, o4);
+            rows ? go(reorder_vt_kernel<128, 128, true>) : go(reorder_vt_kernel<128, 128, false>);
         else if (p.d == 128)
-            hipLaunchKernelGGL((reorder_vt_kernel<128, 64>), grid, dim3(threads), 0, s, p, i4, o4);
+            rows ? go(reorder_vt_kernel<128, 64, true>) : go(reorder_vt_kernel<128, 64, false>);
         else if (p.block == 128)
-            hipLaunchKernelGGL((reorder_vt_kernel<64, 128>), grid, dim3(threads), 0, s, p, i4, o4);
+            rows ? go(reorder_vt_kernel<64, 128, true>) : go(reorder_vt_kernel<64, 128, false>);
         else
-            hipLaunchKernelGGL((reorder_vt_kernel<64, 64>), grid, dim3(threads), 0, s, p, i4, o4);
+            rows ? go(reorder_vt_kernel<64, 64, true>) : go(reorder_vt_kernel<64, 64, false>);
     }
     return hipGetLastError();
 }

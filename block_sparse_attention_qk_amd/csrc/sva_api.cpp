@@ -252,7 +252,7 @@ int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* s
     if (!sva::aligned16(in) || !sva::aligned16(out))
         return set_err(SVA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     if (direction != SVA_FORWARD && direction != SVA_INVERSE && direction != SVA_FORWARD_VT &&
-        direction != SVA_FORWARD_KT)
+        direction != SVA_FORWARD_KT && direction != SVA_ROWS_TO_VT && direction != SVA_ROWS_TO_KT)
         return set_err(SVA_ERR_INVALID_ARG, "unknown reorder direction");
     if (in == out) return set_err(SVA_ERR_INVALID_ARG, "reorder cannot run in place");
     hipError_t e = sva::launch_reorder(plan->dev, static_cast<const uint16_t*>(in),

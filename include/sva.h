@@ -97,6 +97,8 @@ extern "C" {
 #define SVA_INVERSE     1  /* tile order [B,H,Np,d] -> raster [B,N,H,d]      */
 #define SVA_FORWARD_VT  2  /* raster [B,N,H,d] -> V tiles [B,H,nB,block/32,4,d,8] */
 #define SVA_FORWARD_KT  3  /* raster [B,N,H,d] -> K tiles [B,H,nB,block/32,d/16,64,8] */
+#define SVA_ROWS_TO_VT  4  /* tile order [B,H,Np,d] -> V tiles (as SVA_FORWARD_VT) */
+#define SVA_ROWS_TO_KT  5  /* tile order [B,H,Np,d] -> K tiles (as SVA_FORWARD_KT) */
 
 /* ---- output layouts of sva_attention_ex ---- */
 #define SVA_LAYOUT_TILE    0   /* O in tile order [B, H, Np, d], padding rows zero */
@@ -219,7 +221,13 @@ int sva_qk_norm_rope_tiled(sva_plan plan, const void* q, const void* k,
 
 /* Token permutation between raster and 3D-tile order (see direction
  * macros).  Forward writes zeros into the padding rows; the inverse drops
- * them.  `in` and `out` must not overlap. */
+ * them.  SVA_ROWS_TO_KT and SVA_ROWS_TO_VT take K or V already in tile order
+ * [B, H, Np, d] (as SVA_FORWARD writes it) and lay each block out as the
+ * K or V tiles sva_select_blocks and sva_attention read, padding rows zero:
+ * the output equals SVA_FORWARD_KT / SVA_FORWARD_VT of the raster tensor
+ * the rows came from, so a caller holding k_r and v_r in tile order
+ * converts them once and calls the rest of the step unchanged.  `in` and
+ * `out` must not overlap. */
 int sva_reorder(sva_plan plan, const void* in, void* out, int direction, void* stream);
 
 /* Block selection.  q_r: tile order [B, H, Np, d] (SVA_FORWARD of Q');

@@ -211,6 +211,39 @@ def test_reorder_parity(name):
     assert np.array_equal(host(run.buf.o), q)
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "d128_b64", "d64_b128",
+                                  "sub64x4", "heads5_d64"])
+def test_rows_to_tiles(name):
+    """SVA_ROWS_TO_KT / SVA_ROWS_TO_VT: K and V given as tile-order rows
+    [B, H, Np, d] come out as the same K and V tiles that SVA_FORWARD_KT /
+    SVA_FORWARD_VT make from the raster tensors, bit for bit, with the
+    padding rows zeroed whatever the input holds there."""
+    wl, g, perm, meta, (q, k, v, wq, wk), ref = small_case(name)
+    run = GpuRun(wl, q, k, v, wq, wk)
+    plan = run.plan
+    k_r = torch.empty(plan.tile_shape, dtype=torch.bfloat16, device="cuda")
+    v_r = torch.empty_like(k_r)
+    S.sva_reorder(plan, run.k, k_r, S.SVA_FORWARD)
+    S.sva_reorder(plan, run.v, v_r, S.SVA_FORWARD)
+    pad = np.ones(g.Np, bool)
+    pad[perm] = False                                        # positions holding a token
+    pad_idx = torch.from_numpy(np.nonzero(pad)[0]).cuda()
+    if pad_idx.numel():
+        k_r.view(torch.int16)[:, :, pad_idx] = 0x3f80          # 1.0: must not reach the tiles
+        v_r.view(torch.int16)[:, :, pad_idx] = -0x4080         # -1.0
+    want_k = torch.empty(plan.kt_shape, dtype=torch.bfloat16, device="cuda")
+    want_v = torch.empty(plan.vt_shape, dtype=torch.bfloat16, device="cuda")
+    S.sva_reorder(plan, run.k, want_k, S.SVA_FORWARD_KT)
+    S.sva_reorder(plan, run.v, want_v, S.SVA_FORWARD_VT)
+    got_k = torch.full_like(want_k, 7.0)
+    got_v = torch.full_like(want_v, 7.0)
+    S.sva_reorder(plan, k_r, got_k, S.SVA_ROWS_TO_KT)
+    S.sva_reorder(plan, v_r, got_v, S.SVA_ROWS_TO_VT)
+    torch.cuda.synchronize()
+    assert torch.equal(got_k.view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(got_v.view(torch.int16), want_v.view(torch.int16))
+
+
 @pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].sparsity > 0
                                   and not SMALL[n].flags & I.DENSE])
 def test_select_parity(name):
