@@ -338,16 +338,17 @@ def h3_prologue(S, I, np, torch, to_dev):
 def measured_traffic(workload, d, b):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
-    None when there is none for this workload or the attention source has
-    changed since the counters were taken."""
+    None when there is none for this workload or the attention source or its
+    build options have changed since the counters were taken."""
     from block_sparse_attention_qk_amd import profile_traffic as PT
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         res = json.load(f)
-    src = "k_attention.hip"
-    if res.get("sources_sha256", {}).get(src) != PT.source_hashes().get(src):
+    now, then = PT.source_hashes(), res.get("sources_sha256", {})
+    # the attention source and the build options it was compiled with
+    if any(then.get(f) != now.get(f) for f in ("k_attention.hip", "build.py")):
         return None
     for name, e in res.get("kernels", {}).items():
         if name.startswith(f"attn_kernel<{d}, {b}, "):

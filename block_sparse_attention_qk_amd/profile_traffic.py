@@ -13,8 +13,9 @@ is scaled by known bytes / counted bytes of that copy.  The result is the
 average HBM-side bytes per dispatch of every kernel, and, with the
 kernel-trace statistics of the same command, the achieved GB/s.
 
-The json also records the SHA-256 of every HIP source, so a reader (bench.py)
-can tell whether the figures still describe the kernels that are built.
+The json also records the SHA-256 of every HIP source and of the build script
+(its compiler options), so a reader (bench.py) can tell whether the figures
+still describe the kernels that are built.
 """
 
 from __future__ import annotations
@@ -32,8 +33,10 @@ CSRC = os.path.join(PKG, "csrc")
 
 
 def source_hashes() -> dict:
+    """SHA-256 of every kernel source and of build.py (whose per-source
+    compiler options shape the kernels' code as much as the sources do)."""
     out = {}
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(PKG, "build.py")]:
         with open(path, "rb") as f:
             out[os.path.basename(path)] = hashlib.sha256(f.read()).hexdigest()
     return out
