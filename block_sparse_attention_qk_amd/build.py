@@ -67,12 +67,11 @@ def _compile(src: str, debug: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, debug: bool = False) -> str:
-    out_dir, lib = (DEBUG_OUT_DIR, DEBUG_LIB) if debug else (OUT_DIR, LIB)
-    os.makedirs(out_dir, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, debug), srcs))
+def _sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def _link(objs, lib: str, verbose: bool) -> str:
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -82,6 +81,31 @@ def build(verbose: bool = False, debug: bool = False) -> str:
     if verbose:
         print(f"built {lib}")
     return lib
+
+
+def build(verbose: bool = False, debug: bool = False) -> str:
+    out_dir, lib = (DEBUG_OUT_DIR, DEBUG_LIB) if debug else (OUT_DIR, LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = _sources()
+    with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, debug), srcs))
+    return _link(objs, lib, verbose)
+
+
+def build_all(verbose: bool = False) -> tuple:
+    """Both libraries, their objects compiled in one pool (the slowest
+    source of each build overlaps the other's)."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(DEBUG_OUT_DIR, exist_ok=True)
+    srcs = _sources()
+    # the largest sources first, so they do not trail the pool
+    jobs = sorted([(src, dbg) for dbg in (False, True) for src in srcs],
+                  key=lambda j: -os.path.getsize(j[0]))
+    with ThreadPoolExecutor(8) as ex:
+        done = dict(zip(jobs, ex.map(lambda j: _compile(*j), jobs)))
+    rel = _link([done[(src, False)] for src in srcs], LIB, verbose)
+    dbg = _link([done[(src, True)] for src in srcs], DEBUG_LIB, verbose)
+    return rel, dbg
 
 
 if __name__ == "__main__":
