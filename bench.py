@@ -347,8 +347,8 @@ def measured_traffic(workload, d, b):
     with open(path) as f:
         res = json.load(f)
     now, then = PT.source_hashes(), res.get("sources_sha256", {})
-    # the attention source and the build options it was compiled with
-    if any(then.get(f) != now.get(f) for f in ("k_attention.hip", "build.py")):
+    # the attention source and the compiler options it was built with
+    if any(then.get(f) != now.get(f) for f in ("k_attention.hip", "k_attention.hip:flags")):
         return None
     for name, e in res.get("kernels", {}).items():
         if name.startswith(f"attn_kernel<{d}, {b}, "):

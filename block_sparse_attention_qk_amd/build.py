@@ -49,6 +49,21 @@ EXTRA = {
 }
 
 
+def flag_signature(name: str) -> str:
+    """The compiler options of source `name`, without the include path (so
+    the text is the same on every machine): what a kernel's code depends on
+    besides its source."""
+    common, skip = [], False
+    for a in COMMON:
+        if skip:
+            skip = False
+        elif a == "-I":
+            skip = True
+        else:
+            common.append(a)
+    return " ".join(common + EXTRA.get(name, []))
+
+
 def _compile(src: str, debug: bool = False) -> str:
     obj = os.path.join(DEBUG_OUT_DIR if debug else OUT_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON, *(["-DSVA_DEBUG"] if debug else []),

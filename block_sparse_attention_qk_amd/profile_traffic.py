@@ -13,9 +13,9 @@ is scaled by known bytes / counted bytes of that copy.  The result is the
 average HBM-side bytes per dispatch of every kernel, and, with the
 kernel-trace statistics of the same command, the achieved GB/s.
 
-The json also records the SHA-256 of every HIP source and of the build script
-(its compiler options), so a reader (bench.py) can tell whether the figures
-still describe the kernels that are built.
+The json also records the SHA-256 of every HIP source and of its compiler
+options, so a reader (bench.py) can tell whether the figures still describe
+the kernels that are built.
 """
 
 from __future__ import annotations
@@ -33,12 +33,17 @@ CSRC = os.path.join(PKG, "csrc")
 
 
 def source_hashes() -> dict:
-    """SHA-256 of every kernel source and of build.py (whose per-source
-    compiler options shape the kernels' code as much as the sources do)."""
+    """SHA-256 of every kernel source, and of each HIP source's compiler
+    options (key "<source>:flags"), which shape its code as much as the
+    source does."""
+    from block_sparse_attention_qk_amd.build import flag_signature
     out = {}
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(PKG, "build.py")]:
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        name = os.path.basename(path)
         with open(path, "rb") as f:
-            out[os.path.basename(path)] = hashlib.sha256(f.read()).hexdigest()
+            out[name] = hashlib.sha256(f.read()).hexdigest()
+        if name.endswith(".hip"):
+            out[name + ":flags"] = hashlib.sha256(flag_signature(name).encode()).hexdigest()
     return out
 
 

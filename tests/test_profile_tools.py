@@ -61,7 +61,8 @@ def test_traffic_calibration_and_bytes(tmp_path):
     assert e["fetch_bytes"] == pytest.approx(2000.0 * 1024 * 2.0)   # mean KiB per dispatch, scaled
     assert e["write_bytes"] == pytest.approx(500.0 * 1024 * 1.0)
     assert e["traffic_gbs"] == pytest.approx((2000 * 2048 + 500 * 1024) / 2e-3 / 1e9)
-    assert "k_attention.hip" in res["sources_sha256"] and "build.py" in res["sources_sha256"]
+    assert "k_attention.hip" in res["sources_sha256"]
+    assert "k_attention.hip:flags" in res["sources_sha256"]
 
 
 def test_traffic_needs_the_calibration_copy(tmp_path):
@@ -122,3 +123,26 @@ def test_kernel_medians(tmp_path):
     med = PK.read_medians(path)
     assert med[ATTN_SHORT] == pytest.approx(2.0)
     assert med["stream_copy_kernel"] == pytest.approx(2.0)
+
+
+def test_bench_traffic_only_for_the_measured_kernel(monkeypatch):
+    """bench.py reports the committed attention traffic only while the
+    attention source and its compiler options match the hashes the counter
+    summary recorded; any change to either makes it None."""
+    import json
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    with open(os.path.join(root, "profiles", "traffic_wan720p_sp75.json")) as f:
+        rec = json.load(f)
+    want = next(e["traffic_bytes"] for k, e in rec["kernels"].items()
+                if k.startswith("attn_kernel<128, 128, "))
+    now = PT.source_hashes()
+    assert bench.measured_traffic("wan720p_sp75", 128, 128) == pytest.approx(round(want, 0))
+    for f in ("k_attention.hip", "k_attention.hip:flags"):
+        changed = dict(now, **{f: "0" * 64})
+        monkeypatch.setattr(PT, "source_hashes", lambda c=changed: c)
+        assert bench.measured_traffic("wan720p_sp75", 128, 128) is None, f
+    monkeypatch.setattr(PT, "source_hashes", lambda: now)
+    assert bench.measured_traffic("no_such_workload", 128, 128) is None
